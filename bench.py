@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated INT4 paged KV-cache hot path on one MI355X.
+
+One step = the whole hot path over one batch of the Llama-3-8B-shaped layer (16 sequences x
+4096 tokens, 32 query / 8 KV heads, head_dim 128, page size 16, Hadamard block 128, INT4):
+
+  1. rotate-quantize-append of the 16 x 4096 prefill tokens (write path, all 8 KV heads),
+  2. rotate-quantize-append of one new decode token per sequence,
+  3. paged decode attention over 4097 tokens per sequence (read path).
+
+Inputs are seeded synthetic bf16 tensors resident in HBM before timing starts. To keep the
+256 MB Infinity Cache from serving reads, steps rotate over 4 copies of the prefill inputs and
+14 copies of the cache (about 2 GB), and the attention of step i reads the cache copy written
+seven steps earlier. Prints one JSON line (see the keys at the bottom).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged INT4 decode-attn & quant-append HBM GB/s (% of MI355X peak), tokens/s"
+PEAK_HBM_GBPS = 8000.0
+N_INPUT_COPIES = 4
+N_CACHE_COPIES = 14
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-iters", type=int, default=200, help="extra decode-only launches for the decode roofline")
+    return p.parse_args()
+
+
+def append_bytes(tokens: int, heads: int, bits: int, d: int = 128) -> int:
+    """Algorithmic bytes of rotate-quantize-append: bf16 K+V read, codes + fp32 scale/zero
+    written for K and V, plus the int64 slot of every token."""
+    per_token_head = 2 * d * 2 + 2 * d * bits // 8 + 2 * 8
+    return tokens * heads * per_token_head + tokens * 8
+
+
+def decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size: int, d: int = 128) -> int:
+    """Algorithmic bytes of one decode step: K/V codes + scale/zero of every attended token
+    and KV head, the block-table entries read, bf16 q, fp32 out and the context lengths."""
+    per_token_head = 2 * d * bits // 8 + 2 * 8
+    toks = int(np.sum(lens))
+    pages = int(np.sum((np.asarray(lens) + page_size - 1) // page_size))
+    b = len(lens)
+    return toks * num_kv_heads * per_token_head + pages * 4 + b * num_q_heads * d * (2 + 4) + b * 4
+
+
+def cpu_baseline(shape, k, v, slots, plan, q) -> dict:
+    """The CPU oracle, as it stands, on a bounded sample of the same workload."""
+    from oracle import kvq_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    n_seq = 8
+    n_tok = n_seq * shape.context_lens[0]
+    cache = O.PagedCache(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.head_dim, shape.bits)
+    t0 = time.perf_counter()
+    O.append(cache, k[:n_tok], v[:n_tok], slots[:n_tok], shape.hadamard_block, shape.token_scale)
+    t1 = time.perf_counter()
+    lens = np.asarray(shape.context_lens[:n_seq])
+    O.decode(cache, q[:n_seq], plan.block_table[:n_seq], lens, shape.num_kv_heads, shape.hadamard_block)
+    t2 = time.perf_counter()
+    ab = append_bytes(n_tok, shape.num_kv_heads, shape.bits)
+    db = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+    return {
+        "value": round((ab + db) / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"append of {n_tok} prefill tokens x {shape.num_kv_heads} KV heads ({t1 - t0:.1f} s) + decode of "
+                  f"{n_seq} sequences x {shape.num_q_heads} heads over {shape.context_lens[0]} tokens ({t2 - t1:.1f} s)",
+        "append_GBps": round(ab / (t1 - t0) / 1e9, 4), "decode_GBps": round(db / (t2 - t1) / 1e9, 4),
+        "decode_tokens_per_s": round(n_seq / (t2 - t1), 3),
+    }
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and this build has "
+              "no multi-GPU path (see the sharding paragraph of the design notes); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    shape = W.config(args.workload)
+    assert shape.layers == 1 and shape.chunk == 0, "the step benchmark covers single-layer prefill workloads"
+    plan = W.plan_pages(shape, extra_tokens=1)
+    seq, pos = W.prefill_order(shape)
+    k, v = W.draw_kv(shape, len(seq))
+    slots = W.slots_for_positions(plan, shape.page_size, seq, pos)
+    dseq, dpos = W.decode_positions(shape)
+    kn, vn = W.draw_kv(shape, shape.batch, stream="decode")
+    dslots = W.slots_for_positions(plan, shape.page_size, dseq, dpos)
+    q = W.draw_q(shape)
+    lens_dec = np.asarray(shape.context_lens, dtype=np.int32) + 1
+    max_len = int(lens_dec.max())
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_in = [bf16(k)]
+    v_in = [bf16(v)]
+    for _ in range(N_INPUT_COPIES - 1):
+        k_in.append(k_in[0].clone())
+        v_in.append(v_in[0].clone())
+    slots_d = torch.from_numpy(slots).to(dev)
+    kn_d, vn_d, dslots_d = bf16(kn), bf16(vn), torch.from_numpy(dslots).to(dev)
+    q_d = bf16(q)
+    bt_d = torch.from_numpy(plan.block_table).to(dev)
+    lens_d = torch.from_numpy(lens_dec).to(dev)
+    caches = [kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+              for _ in range(N_CACHE_COPIES)]
+    ws_bytes = kvq.decode_workspace_size(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
+                                         shape.page_size)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+    hb, ts = shape.hadamard_block, shape.token_scale
+    stream = torch.cuda.current_stream()
+
+    def prefill(i):
+        kvq.rotate_quantize_append(k_in[i % N_INPUT_COPIES], v_in[i % N_INPUT_COPIES], slots_d,
+                                   caches[i % N_CACHE_COPIES], hb, ts, stream=stream)
+
+    def decode_append(i):
+        kvq.rotate_quantize_append(kn_d, vn_d, dslots_d, caches[i % N_CACHE_COPIES], hb, ts, stream=stream)
+
+    def attend(c):
+        kvq.paged_decode_attention(q_d, caches[c % N_CACHE_COPIES], bt_d, lens_d, max_len, hb, out=out,
+                                   workspace=ws, stream=stream)
+
+    # every cache copy holds a full prefill + decode token before anything is timed
+    for i in range(N_CACHE_COPIES):
+        prefill(i)
+        decode_append(i)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        prefill(i)
+        if ev is not None:
+            ev[1].record(stream)
+        decode_append(i)
+        if ev is not None:
+            ev[2].record(stream)
+        attend(i + N_CACHE_COPIES // 2)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    prefill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dapp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    attn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    # decode attention alone, cycling over the 14 cache copies
+    dec_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_iters)]
+    for i in range(10):
+        attend(i)
+    torch.cuda.synchronize()
+    for i in range(args.decode_iters):
+        dec_ev[i][0].record(stream)
+        attend(i)
+        dec_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_only_ms = np.array([e[0].elapsed_time(e[1]) for e in dec_ev])
+
+    b_prefill = append_bytes(len(seq), shape.num_kv_heads, shape.bits)
+    b_dapp = append_bytes(shape.batch, shape.num_kv_heads, shape.bits)
+    b_attn = decode_bytes(lens_dec, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+    step_bytes = b_prefill + b_dapp + b_attn
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    def gbps(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    pre_avg, attn_avg, dec_avg = float(prefill_ms.mean()), float(attn_ms.mean()), float(dec_only_ms.mean())
+    kernels = {
+        "rotate_quantize_append_prefill": {"bytes": b_prefill, "avg_ms": round(pre_avg, 5),
+                                           "GBps": round(gbps(b_prefill, pre_avg), 1),
+                                           "frac_of_peak": round(gbps(b_prefill, pre_avg) / PEAK_HBM_GBPS, 4),
+                                           "tokens_per_s": round(len(seq) / (pre_avg * 1e-3), 1)},
+        "rotate_quantize_append_decode_token": {"bytes": b_dapp, "avg_ms": round(float(dapp_ms.mean()), 5)},
+        "paged_decode_attention_in_step": {"bytes": b_attn, "avg_ms": round(attn_avg, 5),
+                                           "GBps": round(gbps(b_attn, attn_avg), 1)},
+        "paged_decode_attention_alone": {
+            "bytes": b_attn, "avg_ms": round(dec_avg, 5), "median_ms": round(float(np.median(dec_only_ms)), 5),
+            "p10_ms": round(float(np.percentile(dec_only_ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(dec_only_ms, 90)), 5),
+            "GBps": round(gbps(b_attn, dec_avg), 1), "frac_of_peak": round(gbps(b_attn, dec_avg) / PEAK_HBM_GBPS, 4),
+            "decode_tokens_per_s": round(shape.batch / (dec_avg * 1e-3), 1)},
+    }
+    dominant = "rotate_quantize_append_prefill" if pre_avg >= attn_avg else "paged_decode_attention_alone"
+    dom_bytes, dom_ms = (b_prefill, pre_avg) if dominant.startswith("rotate") else (b_attn, dec_avg)
+    achieved = gbps(dom_bytes, dom_ms)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": dominant,
+                "bytes_per_launch": dom_bytes}
+    roofline_decode = {"bound": "hbm", "achieved": round(gbps(b_attn, dec_avg), 1), "peak": PEAK_HBM_GBPS,
+                       "unit": "GB/s", "frac": round(gbps(b_attn, dec_avg) / PEAK_HBM_GBPS, 4), "traffic": None,
+                       "kernel": "paged_decode_attention", "bytes_per_launch": b_attn}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "storage": f"int{shape.bits} codes + fp32 scale/zero",
+        "data": "synthetic (seeded bf16 K/V/Q: N(0,1), 4 outlier channels x10, per-token LogNormal(0,1) norms)",
+        "config": {"workload": f"{shape.name}: {shape.batch} seq x {shape.context_lens[0]} tokens prefill-append + "
+                               f"1 decode step (append + attention over {max_len}), {shape.num_q_heads}/"
+                               f"{shape.num_kv_heads} heads, head_dim 128, page 16, Hadamard block {hb}, "
+                               f"INT{shape.bits}",
+                   "global_batch": shape.batch, "seq_len": max_len, "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+        "step_bytes": step_bytes,
+        "decode_tokens_per_s": kernels["paged_decode_attention_alone"]["decode_tokens_per_s"],
+        "kernels": kernels, "roofline": roofline, "roofline_decode": roofline_decode,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, k, v, slots, plan, q)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * kvq.h - C ABI of the rotated low-bit paged KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * Two hot paths and one inspection call, all asynchronous on a caller-supplied HIP stream:
+ *
+ *   kvq_rotate_quantize_append   write path: block-diagonal Hadamard rotation of every new
+ *                                K/V head vector, token-wise asymmetric INT4 (or INT2)
+ *                                quantization with a float32 scale and zero per token per
+ *                                head, nibble packing, paged store through a slot mapping.
+ *                                (SAW-INT4 abstract: "SAW-INT4: System-Aware 4-Bit KV-Cache
+ *                                Quantization for Real-World LLM Serving", fugumt.com paper
+ *                                page, Abstract - token-wise INT4 after a block-diagonal
+ *                                Hadamard rotation, fused into a paged cache layout. The
+ *                                optional per-token scaling step before quantization is the
+ *                                S of the OScaR formula V-hat = Quant(S (R V)), zhichai.net
+ *                                "OScaR: Occam's Razor for Extreme KV Cache Quantization in
+ *                                LLMs", section "The OScaR Framework", used at INT2.)
+ *   kvq_paged_decode_attention   read path: one decode query per head attends over its
+ *                                sequence's quantized pages, dequantizing on the fly in the
+ *                                rotated basis (the query is rotated by the same matrix),
+ *                                split over pages with an online-softmax merge; one inverse
+ *                                rotation of the output undoes the rotation of V.
+ *                                (Dequantization fused into attention: ainews.cool
+ *                                "Technical Deep Dive", third phase; a paged low-bit
+ *                                attention kernel: the OSCAR abstract on the
+ *                                thelatestinai.com page; split decoding against which OScaR
+ *                                compares: FlashDecoding-v2, named in the OScaR abstract on
+ *                                the same page.)
+ *   kvq_dequant_page             codes of one page back to float32, optionally un-rotated
+ *                                (inspection and test surface).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is DEVICE memory owned by the caller; the library allocates nothing,
+ *     keeps no global state and may be called from several host threads at once.
+ *   - Each call validates its arguments on the host, enqueues its kernels on `stream` and
+ *     returns; results are valid once the caller synchronises the stream. No call blocks.
+ *   - bf16 values cross the ABI as their 16-bit patterns (uint16_t).
+ *   - Return value: KVQ_OK, or the first failed check (nothing is launched then), or
+ *     KVQ_ERR_HIP if the launch itself failed. No C++ exception crosses the ABI.
+ *   - head_dim must be 128 and page_size a multiple of 16 (KVQ_ERR_UNSUPPORTED otherwise).
+ *
+ * Rotation R (block size b, a power of two dividing head_dim; b = 1 is no rotation, i.e.
+ * plain INT4): R = blockdiag(H_b, ..., H_b) / sqrt(b), H_b the Sylvester Hadamard matrix
+ * H_b[i][j] = (-1)^popcount(i & j), blocks over contiguous channels. R is symmetric and its
+ * own inverse.
+ *
+ * Quantizer (per token, per KV head, per tensor): y = R x in float32; with token_scale,
+ * s = RMS(y) (1 if 0) and u = y / s, else u = y, s = 1; scale_u = (max u - min u) / (2^bits - 1);
+ * code = clamp(rint((u - min u) / scale_u), 0, 2^bits - 1) (round half to even, IEEE divide;
+ * all codes 0 when scale_u = 0). Stored: scale = scale_u * s, zero = min u * s, so that
+ * dequant = code * scale + zero in the rotated basis.
+ *
+ * Cache layout (row = head_dim * bits / 8 bytes; codes packed low bits first, i.e. for INT4
+ * channel 2j is the low nibble of byte j, for INT2 channel 4j + k sits at bits 2k..2k+1):
+ *   K codes  uint8 [num_pages][num_kv_heads][page_size][row]            token-major rows
+ *   V codes  uint8 [num_pages][num_kv_heads][page_size / 4][row][4]     byte j of token t of a
+ *            page-head tile sits at ((t / 4) * row + j) * 4 + t % 4: four consecutive tokens
+ *            are interleaved byte by byte, so a 32-bit word holds one byte of four tokens
+ *   K/V sz   float [num_pages][num_kv_heads][page_size][2] = {scale, zero}
+ *   slot     = page * page_size + offset inside the page.
+ */
+#ifndef KVQ_H_
+#define KVQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef int32_t kvq_status;
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,         /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = 2,        /* a size is negative or inconsistent (e.g. q heads not a multiple of kv heads) */
+  KVQ_ERR_UNSUPPORTED = 3,  /* valid but not implemented: bits not 2/4, head_dim != 128, page_size % 16 */
+  KVQ_ERR_WORKSPACE = 4,    /* decode workspace missing or smaller than kvq_paged_decode_workspace_size */
+  KVQ_ERR_HIP = 5           /* the HIP runtime rejected a launch */
+};
+
+/* KVQ_ABI_VERSION of the loaded library. */
+int32_t kvq_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* kvq_status_string(int32_t status);
+
+/*
+ * Write path: rotate, quantize, pack and append num_tokens new tokens for every KV head.
+ *
+ *   k, v             bf16 [num_tokens][num_kv_heads][head_dim], head vectors contiguous;
+ *                    token i starts at element i * k_token_stride (v_token_stride), both
+ *                    >= num_kv_heads * head_dim.
+ *   slot_mapping     int64 [num_tokens]: destination slot of token i; a negative slot skips
+ *                    the token; slots >= num_pages * page_size are ignored as well. Two
+ *                    tokens with the same slot in one call race (undefined result).
+ *   k_codes, v_codes, k_sz, v_sz   the cache, layout above; only the addressed rows change.
+ *   hadamard_block   b: power of two dividing head_dim (1 = no rotation).
+ *   bits             4 (INT4) or 2 (INT2).
+ *   token_scale      0: SAW-INT4 (rotate, quantize); 1: OScaR (rotate, scale per token, quantize).
+ *
+ * num_tokens == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_rotate_quantize_append(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+    const int64_t* slot_mapping,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_sz, float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    int32_t hadamard_block, int32_t bits, int32_t token_scale,
+    hipStream_t stream);
+
+/*
+ * Bytes of device workspace kvq_paged_decode_attention needs for these sizes (0 when the
+ * call runs unsplit). pages_per_split: 0 = the library's choice, else the number of pages
+ * each split covers. Pass the same values to both calls.
+ */
+size_t kvq_paged_decode_workspace_size(
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t page_size, int32_t pages_per_split);
+
+/*
+ * Read path: one decode step of attention for every (sequence, query head).
+ *
+ *   q                bf16 [batch][num_q_heads][head_dim].
+ *   q_prerotated     0: the kernel forms R q in float32 (the bf16 q is never re-rounded);
+ *                    1: q already holds R q.
+ *   k_codes ... v_sz the cache written by kvq_rotate_quantize_append (same bits, b).
+ *   block_table      int32 [batch][max_pages_per_seq]: physical page of each logical page;
+ *                    only the first ceil(context_lens[i] / page_size) entries are read.
+ *   context_lens     int32 [batch] (device): tokens to attend per sequence, each in
+ *                    [0, max_context_len]; 0 gives a zero output row.
+ *   max_context_len  host-side upper bound of context_lens, used to size the grid.
+ *   num_q_heads      multiple of num_kv_heads; query head h reads KV head h / (num_q_heads / num_kv_heads),
+ *                    at most 8 query heads per KV head.
+ *   softmax_scale    <= 0 selects 1 / sqrt(head_dim).
+ *   out              float32 [batch][num_q_heads][head_dim], un-rotated (R applied once).
+ *   workspace        device scratch of at least kvq_paged_decode_workspace_size(...) bytes
+ *                    (may be NULL when that size is 0); its contents need no initialisation
+ *                    and are meaningless after the call.
+ *   pages_per_split  0 = library's choice; > 0 forces the split size (tuning and tests).
+ *
+ * batch == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_paged_decode_attention(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream);
+
+/*
+ * Dequantize every token of one page of the K (tensor = 0) or V (tensor = 1) half of the
+ * cache: out float32 [num_kv_heads][page_size][head_dim] = code * scale + zero (a single
+ * rounding), multiplied by R^T when unrotate = 1. page must lie in [0, num_pages).
+ */
+kvq_status kvq_dequant_page(
+    const uint8_t* codes, const float* sz, int32_t tensor, int32_t page, int32_t num_pages,
+    int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, int32_t unrotate,
+    float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H_ */

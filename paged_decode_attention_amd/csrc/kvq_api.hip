@@ -1,0 +1,196 @@
+// C ABI of libkvq: argument validation, workspace sizing and kernel launches. Host code only;
+// every kernel lives in kvq_append.hip, kvq_decode.hip and kvq_dequant.hip.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/kvq.h"
+#include "kvq_launch.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+kvq_status check_common(int32_t head_dim, int32_t page_size, int32_t hadamard_block, int32_t bits) {
+  if (page_size <= 0 || hadamard_block <= 0) return KVQ_ERR_SHAPE;
+  if (bits != 2 && bits != 4) return KVQ_ERR_UNSUPPORTED;
+  if (head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (page_size % kvq::kTileTokens) return KVQ_ERR_UNSUPPORTED;
+  if (!is_pow2(hadamard_block) || head_dim % hadamard_block) return KVQ_ERR_SHAPE;
+  return KVQ_OK;
+}
+
+float inv_sqrt(int32_t b) { return static_cast<float>(1.0 / std::sqrt(static_cast<double>(b))); }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WorkspaceLayout {
+  size_t acc_bytes, ml_offset, total;
+};
+
+WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_q_heads) {
+  WorkspaceLayout w{0, 0, 0};
+  if (num_splits <= 1) return w;
+  const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
+  w.acc_bytes = rows * kvq::kHeadDim * sizeof(float);
+  w.ml_offset = round_up(w.acc_bytes);
+  w.total = w.ml_offset + round_up(rows * 2 * sizeof(float));
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "invalid or inconsistent size, stride, block size or alignment";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (bits must be 2 or 4, head_dim 128, page_size a multiple of 16, at most 8 query heads per KV head)";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+kvq_status kvq_rotate_quantize_append(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+    const int64_t* slot_mapping,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_sz, float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    int32_t hadamard_block, int32_t bits, int32_t token_scale,
+    hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
+  if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
+  if (token_scale != 0 && token_scale != 1) return KVQ_ERR_SHAPE;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (k_token_stride < row_elems || v_token_stride < row_elems) return KVQ_ERR_SHAPE;
+  if (k_token_stride % 8 || v_token_stride % 8) return KVQ_ERR_SHAPE;
+  if (num_kv_heads > 65535 || (num_tokens + 15) / 16 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping || !k_codes || !v_codes || !k_sz || !v_sz) return KVQ_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(k_codes, 4) ||
+      !aligned(v_codes, 4) || !aligned(k_sz, 8) || !aligned(v_sz, 8))
+    return KVQ_ERR_SHAPE;
+
+  kvq::AppendArgs a{};
+  a.k = k;
+  a.v = v;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.slots = slot_mapping;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_sz = k_sz;
+  a.v_sz = v_sz;
+  a.num_slots = static_cast<int64_t>(num_pages) * page_size;
+  a.page_size = page_size;
+  a.hb = hadamard_block;
+  a.inv_sqrt_hb = inv_sqrt(hadamard_block);
+  a.bits = bits;
+  a.token_scale = token_scale;
+  return kvq::launch_append(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t page_size, int32_t pages_per_split) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kvq::kHeadDim || page_size <= 0 ||
+      max_context_len < 0 || pages_per_split < 0)
+    return 0;
+  const kvq::SplitPlan p = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  return workspace_layout(p.num_splits, batch, num_q_heads).total;
+}
+
+kvq_status kvq_paged_decode_attention(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
+      max_pages_per_seq < 0 || pages_per_split < 0)
+    return KVQ_ERR_SHAPE;
+  if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
+  if (num_q_heads % num_kv_heads) return KVQ_ERR_SHAPE;
+  if (q_prerotated != 0 && q_prerotated != 1) return KVQ_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
+  if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !k_codes || !v_codes || !k_sz || !v_sz || !block_table || !context_lens || !out) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_sz, 8) ||
+      !aligned(v_sz, 8) || !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return KVQ_ERR_SHAPE;
+
+  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
+
+  kvq::DecodeArgs a{};
+  a.q = q;
+  a.q_prerotated = q_prerotated;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_sz = k_sz;
+  a.v_sz = v_sz;
+  a.page_size = page_size;
+  a.block_table = block_table;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_pages = num_pages;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.hb = hadamard_block;
+  a.inv_sqrt_hb = inv_sqrt(hadamard_block);
+  a.bits = bits;
+  const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
+  a.qk_scale_log2 = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
+  a.out = out;
+  a.num_splits = plan.num_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ws_acc = ws.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
+  return kvq::launch_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_dequant_page(
+    const uint8_t* codes, const float* sz, int32_t tensor, int32_t page, int32_t num_pages,
+    int32_t num_kv_heads, int32_t page_size, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, int32_t unrotate,
+    float* out, hipStream_t stream) {
+  if (num_kv_heads <= 0 || num_pages <= 0 || page < 0 || page >= num_pages) return KVQ_ERR_SHAPE;
+  if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
+  if ((tensor != 0 && tensor != 1) || (unrotate != 0 && unrotate != 1)) return KVQ_ERR_SHAPE;
+  if (num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!codes || !sz || !out) return KVQ_ERR_NULL;
+  if (!aligned(codes, 4) || !aligned(sz, 8) || !aligned(out, 16)) return KVQ_ERR_SHAPE;
+  kvq::DequantArgs a{};
+  a.codes = codes;
+  a.sz = sz;
+  a.tensor = tensor;
+  a.page = page;
+  a.num_kv_heads = num_kv_heads;
+  a.page_size = page_size;
+  a.hb = hadamard_block;
+  a.inv_sqrt_hb = inv_sqrt(hadamard_block);
+  a.bits = bits;
+  a.unrotate = unrotate;
+  a.out = out;
+  return kvq::launch_dequant(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+"""The C ABI on the host, without a GPU: the library loads, exports every entry point that
+include/kvq.h declares, and rejects invalid arguments with the documented status before any
+launch (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_decode_attention_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = _declared()
+    assert set(names) == set(kvq.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert kvq.abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert kvq.status_string(s)
+    assert kvq.status_string(99) == "unknown status"
+
+
+NULL = None
+
+
+def _append(**kw):
+    a = dict(k=NULL, v=NULL, ks=1024, vs=1024, n=4, h=8, d=128, slots=NULL, kc=NULL, vc=NULL, ksz=NULL, vsz=NULL,
+             pages=10, ps=16, hb=32, bits=4, ts=0)
+    a.update(kw)
+    return kvq.lib().kvq_rotate_quantize_append(a["k"], a["v"], a["ks"], a["vs"], a["n"], a["h"], a["d"], a["slots"],
+                                                a["kc"], a["vc"], a["ksz"], a["vsz"], a["pages"], a["ps"], a["hb"],
+                                                a["bits"], a["ts"], NULL)
+
+
+def test_append_validation():
+    assert _append(n=0) == kvq.KVQ_OK                       # no-op before pointer checks
+    assert _append() == kvq.KVQ_ERR_NULL
+    assert _append(n=-1) == kvq.KVQ_ERR_SHAPE
+    assert _append(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(bits=8) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(d=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(ps=8) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _append(ps=0) == kvq.KVQ_ERR_SHAPE
+    assert _append(hb=3) == kvq.KVQ_ERR_SHAPE
+    assert _append(hb=256) == kvq.KVQ_ERR_SHAPE
+    assert _append(hb=0) == kvq.KVQ_ERR_SHAPE
+    assert _append(ts=2) == kvq.KVQ_ERR_SHAPE
+    assert _append(ks=1000) == kvq.KVQ_ERR_SHAPE           # shorter than H * D
+    assert _append(ks=1028) == kvq.KVQ_ERR_SHAPE           # not a multiple of 8 elements
+    assert _append(h=0) == kvq.KVQ_ERR_SHAPE
+    for hb in (1, 2, 4, 8, 16, 32, 64, 128):
+        assert _append(hb=hb) == kvq.KVQ_ERR_NULL           # valid sizes: only the pointers are missing
+
+
+def _decode(**kw):
+    a = dict(q=NULL, pre=0, kc=NULL, vc=NULL, ksz=NULL, vsz=NULL, pages=100, ps=16, bt=NULL, mpps=64, cl=NULL,
+             mcl=1024, b=2, hq=32, hkv=8, d=128, hb=128, bits=4, scale=0.0, out=NULL, ws=NULL, wsb=0, pps=0)
+    a.update(kw)
+    return kvq.lib().kvq_paged_decode_attention(
+        a["q"], a["pre"], a["kc"], a["vc"], a["ksz"], a["vsz"], a["pages"], a["ps"], a["bt"], a["mpps"], a["cl"],
+        a["mcl"], a["b"], a["hq"], a["hkv"], a["d"], a["hb"], a["bits"], a["scale"], a["out"], a["ws"], a["wsb"],
+        a["pps"], NULL)
+
+
+def test_decode_validation():
+    assert _decode(b=0) == kvq.KVQ_OK
+    assert _decode() == kvq.KVQ_ERR_NULL
+    assert _decode(hq=30) == kvq.KVQ_ERR_SHAPE              # not a multiple of kv heads
+    assert _decode(hq=72) == kvq.KVQ_ERR_UNSUPPORTED        # 9 query heads per kv head
+    assert _decode(bits=1) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(d=256) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _decode(hb=48) == kvq.KVQ_ERR_SHAPE
+    assert _decode(mpps=10) == kvq.KVQ_ERR_SHAPE            # block table narrower than max_context_len needs
+    assert _decode(mcl=-1) == kvq.KVQ_ERR_SHAPE
+    assert _decode(pre=2) == kvq.KVQ_ERR_SHAPE
+    assert _decode(pps=-3) == kvq.KVQ_ERR_SHAPE
+    assert _decode(b=-1) == kvq.KVQ_ERR_SHAPE
+
+
+def test_workspace_size():
+    L = kvq.lib()
+    # unsplit: no workspace
+    assert L.kvq_paged_decode_workspace_size(256, 32, 8, 128, 8192, 16, 0) == 0
+    w = L.kvq_paged_decode_workspace_size(1, 32, 8, 128, 8192, 16, 0)
+    assert w > 0
+    # forced split size: splits = ceil(512 / 64) = 8 -> 8 * 32 * 130 floats at least
+    w8 = L.kvq_paged_decode_workspace_size(1, 32, 8, 128, 8192, 16, 64)
+    assert w8 >= 8 * 32 * 130 * 4
+    assert L.kvq_paged_decode_workspace_size(1, 32, 8, 128, 8192, 16, 512) == 0   # one split
+    assert L.kvq_paged_decode_workspace_size(0, 32, 8, 128, 8192, 16, 0) == 0
+
+
+def test_dequant_validation():
+    L = kvq.lib()
+    f = lambda **kw: L.kvq_dequant_page(NULL, NULL, kw.get("t", 0), kw.get("page", 0), kw.get("pages", 4), 8, 16, 128,
+                                        kw.get("hb", 32), kw.get("bits", 4), kw.get("un", 0), NULL, NULL)
+    assert f() == kvq.KVQ_ERR_NULL
+    assert f(page=4) == kvq.KVQ_ERR_SHAPE
+    assert f(page=-1) == kvq.KVQ_ERR_SHAPE
+    assert f(t=2) == kvq.KVQ_ERR_SHAPE
+    assert f(un=5) == kvq.KVQ_ERR_SHAPE
+    assert f(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    c = kvq.PagedKVCache.empty(4, 2, 16, 4, device="cpu")
+    with pytest.raises(ValueError):
+        kvq.dequant_page(c, "k", 0, 32)
