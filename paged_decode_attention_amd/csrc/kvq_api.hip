@@ -41,6 +41,75 @@ WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_
 
 }  // namespace
 
+namespace kvq {
+
+// Builds the lane plan of the cross-lane Walsh-Hadamard stages by running the butterfly network
+// symbolically on the unit vectors of one block of lanes (see RowFwhtPlan).
+RowFwhtPlan make_row_fwht_plan(int32_t hb) {
+  RowFwhtPlan p{};
+  p.hb = hb;
+  p.inv_sqrt_hb = inv_sqrt(hb);
+  uint64_t identity = 0;
+  for (int l = 0; l < 16; ++l) identity |= static_cast<uint64_t>(l) << (4 * l);
+  p.pos = identity;
+  const int nl = hb >= 16 ? hb / 8 : 1;  // lanes per block
+  int n = 0;
+  while ((1 << n) < nl) ++n;
+  p.lane_stages = n;
+  if (n == 0) return p;
+  auto parity = [](int x) { return __builtin_popcount(static_cast<unsigned>(x)) & 1; };
+  static const int kMasks[4] = {1, 2, 7, 8};
+  int dual[4] = {0, 0, 0, 0};  // functional f_k with f_k(m_j) = [j == k]: lane l is an "a" lane iff f_k(l) = 0
+  for (int k = 0; k < n; ++k) {
+    for (int f = 0; f < nl; ++f) {
+      bool ok = true;
+      for (int j = 0; j < n; ++j) ok = ok && (parity(f & kMasks[j]) == (j == k ? 1 : 0));
+      if (ok) {
+        dual[k] = f;
+        break;
+      }
+    }
+  }
+  int v[16][16] = {};  // true value of lane l as +-1 coefficients over the block's inputs
+  int sig[16];
+  for (int l = 0; l < nl; ++l) {
+    v[l][l] = 1;
+    sig[l] = 1;
+  }
+  for (int k = 0; k < n; ++k) {
+    const int m = kMasks[k];
+    int nv[16][16], nsig[16];
+    for (int l = 0; l < nl; ++l) {
+      const bool a = parity(dual[k] & l) == 0;
+      const int c = (a ? 1 : -1) * sig[l] * sig[l ^ m];
+      if (c < 0)
+        for (int blk = 0; blk < 16; blk += nl) p.neg[k] |= 1u << (blk + l);
+      nsig[l] = a ? sig[l] : -sig[l];
+      for (int i = 0; i < nl; ++i) nv[l][i] = (c * sig[l ^ m] * v[l ^ m][i] + sig[l] * v[l][i]) * nsig[l];
+    }
+    for (int l = 0; l < nl; ++l) {
+      sig[l] = nsig[l];
+      for (int i = 0; i < nl; ++i) v[l][i] = nv[l][i];
+    }
+  }
+  p.pos = 0;
+  for (int l = 0; l < nl; ++l) {
+    int row = -1;
+    for (int r = 0; r < nl && row < 0; ++r) {
+      bool eq = true;
+      for (int i = 0; i < nl; ++i) eq = eq && (v[l][i] == (parity(r & i) ? -1 : 1));
+      if (eq) row = r;
+    }
+    for (int blk = 0; blk < 16; blk += nl) {
+      p.pos |= static_cast<uint64_t>(blk + row) << (4 * (blk + l));
+      if (sig[l] < 0) p.sign |= 1u << (blk + l);
+    }
+  }
+  return p;
+}
+
+}  // namespace kvq
+
 extern "C" {
 
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
@@ -92,8 +161,7 @@ kvq_status kvq_rotate_quantize_append(
   a.v_sz = v_sz;
   a.num_slots = static_cast<int64_t>(num_pages) * page_size;
   a.page_size = page_size;
-  a.hb = hadamard_block;
-  a.inv_sqrt_hb = inv_sqrt(hadamard_block);
+  a.rot = kvq::make_row_fwht_plan(hadamard_block);
   a.bits = bits;
   a.token_scale = token_scale;
   return kvq::launch_append(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

@@ -15,15 +15,13 @@
 namespace kvq {
 namespace {
 
-// Rotate, optionally scale per token, quantize and pack the 8 channels this lane holds.
-// Returns the packed codes (INT4: 32 bits, INT2: low 16 bits); scale/zero are the stored
-// (already un-scaled) values, identical in all 16 lanes of the group.
+// Rotate, optionally scale per token, quantize and pack the 8 channels this lane holds (output
+// block lf.pos of the rotated vector). Returns the packed codes (INT4: 32 bits, INT2: low 16
+// bits); scale/zero are the stored values, identical in all 16 lanes of the group.
 template <int BITS, bool TOKEN_SCALE>
-__device__ __forceinline__ uint32_t rotate_quantize8(float (&x)[8], int hb, float inv_sqrt_hb, int li,
+__device__ __forceinline__ uint32_t rotate_quantize8(float (&x)[8], const RowFwhtPlan& rot, const LaneFwht& lf,
                                                      float& scale, float& zero) {
-  fwht_row16(x, hb, li);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] *= inv_sqrt_hb;
+  fwht_row16_planned(x, rot, lf);
 
   float s = 1.0f;
   if constexpr (TOKEN_SCALE) {
@@ -35,28 +33,35 @@ __device__ __forceinline__ uint32_t rotate_quantize8(float (&x)[8], int hb, floa
     ss = row16_sum_f64(ss);
     s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
     if (s == 0.0f) s = 1.0f;
+    const float rs = 1.0f / s;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = x[k] / s;
+    for (int k = 0; k < 8; ++k) x[k] = div_rn(x[k], s, rs);
   }
 
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int k = 1; k < 8; ++k) {
-    mn = fminf(mn, x[k]);
-    mx = fmaxf(mx, x[k]);
-  }
+  float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   mn = row16_min(mn);
   mx = row16_max(mx);
   constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
-  const float delta = (mx - mn) / kQmax;  // IEEE division (build uses correctly rounded f32 divide)
+  const float delta = (mx - mn) / kQmax;  // IEEE division (the build uses correctly rounded f32 divide)
 
   uint32_t packed = 0;
   if (delta != 0.0f) {
+    const float r = 1.0f / delta;
+    float c[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float t = (x[k] - mn) / delta;
-      const float c = fminf(fmaxf(rintf(t), 0.0f), kQmax);  // round half to even, then clamp
-      packed |= static_cast<uint32_t>(c) << (BITS * k);
+    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(rintf(div_rn(x[k] - mn, delta, r)), 0.0f), kQmax);
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        packed = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * m + 1], 16.0f, c[2 * m]), m, packed);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float b = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[4 * m + 3], 4.0f, c[4 * m + 2]), 4.0f,
+                                                      c[4 * m + 1]), 4.0f, c[4 * m]);
+        packed = __builtin_amdgcn_cvt_pk_u8_f32(b, m, packed);
+      }
     }
   }
   scale = delta * s;
@@ -109,17 +114,18 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
   bf16x8_to_f32(vw, vx);
 
   // Every lane runs the transform (the DPP exchanges need all 64 lanes); dead rows store nothing.
+  const LaneFwht lf = lane_fwht(a.rot, li);
   float ks, kz, vs, vz;
-  const uint32_t kp = rotate_quantize8<BITS, TOKEN_SCALE>(kx, a.hb, a.inv_sqrt_hb, li, ks, kz);
-  const uint32_t vp = rotate_quantize8<BITS, TOKEN_SCALE>(vx, a.hb, a.inv_sqrt_hb, li, vs, vz);
+  const uint32_t kp = rotate_quantize8<BITS, TOKEN_SCALE>(kx, a.rot, lf, ks, kz);
+  const uint32_t vp = rotate_quantize8<BITS, TOKEN_SCALE>(vx, a.rot, lf, vs, vz);
 
   if (live) {
     const int64_t page = slot / a.page_size;
     const int off = static_cast<int>(slot - page * a.page_size);
     const int64_t tile_index = page * a.num_kv_heads + h;     // (page, head) tile
     const int64_t row_index = tile_index * a.page_size + off;  // (page, head, offset) row
-    store_k<BITS>(a.k_codes + row_index * kRow, li, kp);
-    store_v<BITS>(a.v_codes + tile_index * a.page_size * kRow, off, li, vp);
+    store_k<BITS>(a.k_codes + row_index * kRow, lf.pos, kp);
+    store_v<BITS>(a.v_codes + tile_index * a.page_size * kRow, off, lf.pos, vp);
     if (li == 0) {
       reinterpret_cast<float2*>(a.k_sz)[row_index] = make_float2(ks, kz);
       reinterpret_cast<float2*>(a.v_sz)[row_index] = make_float2(vs, vz);

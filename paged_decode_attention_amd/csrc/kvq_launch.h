@@ -11,6 +11,22 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kTileTokens = 16;   // tokens handled per page sub-tile; page_size % 16 == 0
 
+// Cross-lane part of the Walsh-Hadamard transform of one 16-lane row (8 channels per lane).
+// The lane butterflies use the lane masks 1, 2, 7 and 8 - each a single DPP move (quad_perm,
+// quad_perm, row_half_mirror, row_ror:8) - and every lane keeps its value multiplied by a
+// known sign, so each stage is one fused multiply-add: x = c_stage * x[lane ^ mask] + x. After
+// the last stage lane l holds sign(l) * (Sylvester output block pos(l)). Built on the host by
+// make_row_fwht_plan() for a block size b (b <= 8: no lane stages).
+struct RowFwhtPlan {
+  int32_t hb;            // block size b
+  int32_t lane_stages;   // log2(b / 8) for b >= 16, else 0
+  float inv_sqrt_hb;     // float32(1 / sqrt(b))
+  uint32_t neg[4];       // bit l: stage coefficient of lane l is -1
+  uint32_t sign;         // bit l: lane l ends with the negated output
+  uint64_t pos;          // 4 bits per lane: output channel block (channels 8 pos .. 8 pos + 7)
+};
+RowFwhtPlan make_row_fwht_plan(int32_t hb);
+
 struct AppendArgs {
   const uint16_t* k;
   const uint16_t* v;
@@ -24,8 +40,7 @@ struct AppendArgs {
   float* v_sz;
   int64_t num_slots;              // num_pages * page_size
   int32_t page_size;
-  int32_t hb;                     // Hadamard block
-  float inv_sqrt_hb;              // float32(1 / sqrt(hb))
+  RowFwhtPlan rot;                // the rotation (Hadamard block size and lane plan)
   int32_t bits;
   int32_t token_scale;
 };
