@@ -9,6 +9,8 @@ objects are linked into ``paged_decode_attention_amd/libkvq.so``. Flags:
                                               match a correctly rounded reference bit for bit)
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                               no packed-FP32 VALU instructions
+  -mllvm -amdgpu-mfma-vgpr-form               MFMA accumulators in VGPRs, so the VALU work on
+                                              them (Horner shifts, rescaling) needs no copies
 """
 from __future__ import annotations
 
@@ -23,13 +25,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_dequant.hip"]
+SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_dequant.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

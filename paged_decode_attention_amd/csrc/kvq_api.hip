@@ -2,6 +2,8 @@
 // every kernel lives in kvq_append.hip, kvq_decode.hip and kvq_dequant.hip.
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "../../include/kvq.h"
 #include "kvq_launch.h"
@@ -224,7 +226,14 @@ kvq_status kvq_paged_decode_attention(
   a.num_kv_heads = num_kv_heads;
   a.hb = hadamard_block;
   a.inv_sqrt_hb = inv_sqrt(hadamard_block);
+  a.rot = kvq::make_row_fwht_plan(hadamard_block);
   a.bits = bits;
+  {
+    // KVQ_DECODE_KERNEL=valu selects the VALU kernel (for side-by-side measurements); the
+    // matrix-core kernel is the default.
+    const char* sel = std::getenv("KVQ_DECODE_KERNEL");
+    a.use_valu = (sel && std::strcmp(sel, "valu") == 0) ? 1 : 0;
+  }
   const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
   a.qk_scale_log2 = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
   a.out = out;

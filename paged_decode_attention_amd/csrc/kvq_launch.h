@@ -61,8 +61,10 @@ struct DecodeArgs {
   int32_t batch, num_q_heads, num_kv_heads;
   int32_t hb;
   float inv_sqrt_hb;
+  RowFwhtPlan rot;                // lane plan of the rotation (MFMA kernel)
   int32_t bits;
   float qk_scale_log2;            // softmax_scale * log2(e)
+  int32_t use_valu;               // 1: VALU kernel instead of the MFMA kernel (comparison runs)
   float* out;
   int32_t num_splits;             // splits of the page range per (sequence, kv head)
   int32_t pages_per_split;
@@ -86,6 +88,7 @@ struct DequantArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 
 // Split plan used by both the workspace query and the launch.

@@ -111,15 +111,22 @@ def test_decode_page_table_invariance_and_determinism():
 
 
 def test_decode_split_invariance():
+    """Split counts 1 (auto here), many and few give the same attention: each meets the oracle
+    bound, and they agree with each other to 1e-3. They are not bit-identical: every split runs its
+    own online softmax against its own running maximum, so p * delta - fed to the matrix cores as a
+    bf16 hi + lo pair (about 2^-17 relative rounding) - rounds differently per split."""
     shape = W.config("llama2_70b", batch=1)
     lens = (2000,)
     _say("decode split invariance")
     s, plan, cache = _oracle_cache(shape, lens)
     dev = H.upload_cache(cache)
     q = W.draw_q(s)
+    ref = O.decode(cache, q, plan.block_table, np.array(lens), s.num_kv_heads, s.hadamard_block)
     outs = [_gpu_decode(s, plan, dev, q, lens, pps=p) for p in (0, 1, 7, 125)]
+    for p, o in zip((0, 1, 7, 125), outs):
+        H.check_attention(o, ref, f"pps{p}")
     for o in outs[1:]:
-        assert np.all(H.rel_l2(o, outs[0]) < 1e-5)
+        assert np.all(H.rel_l2(o, outs[0]) < 1e-3)
 
 
 @pytest.mark.parametrize("tensor", ["k", "v"])
