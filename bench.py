@@ -134,7 +134,7 @@ def main():
               for _ in range(N_CACHE_COPIES)]
     ws_bytes = kvq.decode_workspace_size(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
                                          shape.page_size)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws = kvq.decode_workspace(ws_bytes, dev)
     out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
     hb, ts = shape.hadamard_block, shape.token_scale
     stream = torch.cuda.current_stream()

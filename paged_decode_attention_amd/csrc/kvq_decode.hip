@@ -281,8 +281,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.num_q_heads / a.num_kv_heads;
   const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads),
                   static_cast<unsigned>(a.batch));
-  hipError_t e = !a.use_valu ? launch_decode_mfma(a, stream)
-                 : (a.bits == 4) ? launch_valu_bits<4>(a, g, grid, stream) : launch_valu_bits<2>(a, g, grid, stream);
+  if (!a.use_valu) return launch_decode_mfma(a, stream);  // launches its own merge
+  hipError_t e = (a.bits == 4) ? launch_valu_bits<4>(a, g, grid, stream) : launch_valu_bits<2>(a, g, grid, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(static_cast<unsigned>((pairs + 3) / 4)), dim3(64), 0, stream, a);

@@ -38,6 +38,22 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kNegInf = -__builtin_inff();
+
+// Page table and context lengths are read-only for the whole call: reading them through the
+// constant address space lets the compiler use scalar loads (waited on with lgkmcnt), so looking
+// up the next pages never waits for the tile loads already in flight (vmcnt).
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int32_t ro_load(const int32_t* p, int64_t i) {
+  return ((const_i32*)(p))[i];
+}
+
+// Orders this wave's LDS writes before its later LDS reads (one-wave workgroups: no s_barrier,
+// and no wait on the global loads in flight).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 constexpr float kLazyRescale = 8.0f;  // log2 units
 __device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
 
@@ -122,41 +138,53 @@ __device__ __forceinline__ uint32_t v_bf16_low_bytes(const uint4 w, int m) {
   }
 }
 
-struct TileLoad {
-  uint4 k;        // K codes: token n, channels 32G..32G+31
-  uint4 v;        // V codes: tokens 4G..4G+3, channels 8n..8n+7
-  float4 ksz01, ksz23;  // (scale, zero) of tokens 4G..4G+3
-  float4 vsz01, vsz23;
+// One 16-token tile as this lane loads it: K codes of token n (channels 32G..32G+31), V codes of
+// tokens 4G..4G+3 (channels 8n..8n+7), and one float of the tile's scale/zero block (lanes 0..31:
+// the 32 K floats, lanes 32..63: the 32 V floats), staged through LDS before use.
+struct TileCodes {
+  uint4 k;
+  uint4 v;
+  float sz;
+};
+
+// Buffer resource over one page-head tile (base and size are wave-uniform, so they live in
+// SGPRs; loads outside the tile would return zero). The last word is the raw-buffer format used
+// for untyped loads on CDNA.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// Per-lane byte offsets of the tile loads (constant for the whole walk).
+struct LaneOffsets {
+  uint32_t k, v;       // inside the K / V tile
+  const float* sz;     // this lane's scale/zero array (K for lanes 0..31, V for 32..63) + lane offset
 };
 
 template <int BITS>
-__device__ __forceinline__ TileLoad load_tile(const DecodeArgs& a, int64_t page, int sub, int kvh, int G, int n) {
+__device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t page, int sub, int kvh,
+                                               const LaneOffsets& lo) {
   constexpr int kRow = kHeadDim * BITS / 8;
-  const int64_t tile = page * a.num_kv_heads + kvh;
-  const uint8_t* kt = a.k_codes + (tile * a.page_size + 16 * sub) * kRow;
-  const uint8_t* vt = a.v_codes + (tile * a.page_size + 16 * sub) * kRow;
-  const float4* ks = reinterpret_cast<const float4*>(a.k_sz + (tile * a.page_size + 16 * sub + 4 * G) * 2);
-  const float4* vs = reinterpret_cast<const float4*>(a.v_sz + (tile * a.page_size + 16 * sub + 4 * G) * 2);
-  TileLoad t;
+  const int64_t row0 = (page * a.num_kv_heads + kvh) * a.page_size + 16 * sub;  // first token row
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + row0 * kRow, 16 * kRow);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + row0 * kRow, 16 * kRow);
+  TileCodes t;
   if constexpr (BITS == 4) {
-    t.k = *reinterpret_cast<const uint4*>(kt + n * kRow + 16 * G);
-    t.v = *reinterpret_cast<const uint4*>(vt + G * 4 * kRow + 16 * n);
+    t.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k, 0, 0));
+    t.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lo.v, 0, 0));
   } else {
-    const uint2 k2 = *reinterpret_cast<const uint2*>(kt + n * kRow + 8 * G);
-    const uint2 v2 = *reinterpret_cast<const uint2*>(vt + G * 4 * kRow + 8 * n);
+    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(kr, lo.k, 0, 0));
+    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, lo.v, 0, 0));
     t.k = make_uint4(k2.x, k2.y, 0, 0);
     t.v = make_uint4(v2.x, v2.y, 0, 0);
   }
-  t.ksz01 = ks[0];
-  t.ksz23 = ks[1];
-  t.vsz01 = vs[0];
-  t.vsz23 = vs[1];
+  t.sz = lo.sz[row0 * 2];
   return t;
 }
 
-template <int BITS>
+template <int BITS, bool PS16>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   __shared__ float qs[8][kHeadDim];
+  __shared__ float4 szs[4][16];  // scale/zero of the four tiles in flight: [tile][K floats 0..31 | V floats 32..63]
 
   const int lane = threadIdx.x;
   const int G = lane >> 4;
@@ -165,16 +193,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int g = a.num_q_heads / a.num_kv_heads;
-  const int ps = a.page_size;
-  const int tiles_per_page = ps / 16;
-  const int len = min(max(a.context_lens[b], 0), a.max_context_len);
+  const int ps = PS16 ? 16 : a.page_size;
+  const int tiles_per_page = PS16 ? 1 : ps / 16;
+  const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + ps - 1) / ps;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(n_pages, p_begin + a.pages_per_split);
   const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g) * kHeadDim;
 
   if (p_begin >= p_end) {
-    if (a.num_splits == 1) {  // empty sequence, unsplit: zero output
+    if (a.num_splits == 1) {  // empty sequence: zero output
       for (int h = G; h < g; h += 4) {
         float4* o = reinterpret_cast<float4*>(a.out + q_row0 + h * kHeadDim + n * 8);
         o[0] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -184,13 +212,60 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     return;
   }
 
+  // ---- walk the split's tiles, four per step, the next four loading meanwhile
+  const int tile_begin = p_begin * tiles_per_page;
+  const int tile_end = min(p_end * tiles_per_page, (len + 15) / 16);
+  const int full_end = min(tile_end, len / 16);  // tiles before this one are entirely valid
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
+
+  v4f acc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf;   // running maximum of head n (log2 units), equal in the 4 lanes of head n
+  float l_part = 0.f;      // this lane's share of sum p (head n)
+  float z_part = 0.f;      // this lane's share of sum p (z - B delta) (head n)
+  const float lazy = kLazyRescale;
+
+  // Page of a tile (scalar load). Tiles past the split's end read the last tile again - an L2 hit,
+  // masked out through pg = -1 - so that every fetch issues the same loads and the wait for a
+  // buffer never has to drain the loads of the next one.
+  LaneOffsets lo;
+  lo.k = (BITS == 4) ? (n * (kHeadDim / 2) + 16 * G) : (n * (kHeadDim / 4) + 8 * G);
+  lo.v = (BITS == 4) ? (G * 4 * (kHeadDim / 2) + 16 * n) : (G * 4 * (kHeadDim / 4) + 8 * n);
+  lo.sz = (lane < 32) ? a.k_sz + lane : a.v_sz + (lane - 32);
+  const int last_tile = tile_end - 1;
+  auto fetch = [&](int t, TileCodes (&x)[4], int64_t (&pg)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tt = min(t + u, last_tile);
+      const int32_t p = ro_load(bt, PS16 ? tt : tt / tiles_per_page);
+      const bool ok = (p >= 0 && p < a.num_pages);
+      pg[u] = (ok && t + u <= last_tile) ? p : -1;
+      x[u] = load_tile<BITS>(a, ok ? p : 0, PS16 ? 0 : tt % tiles_per_page, kvh, lo);
+    }
+  };
+
+  // The query rows (row group G: heads G and G + 4) and then the first four tiles start loading
+  // before the query is prepared; every lane loads (heads past the group re-read the last one).
+  uint4 qw[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int h = min(4 * r + G, g - 1);
+    qw[r] = *reinterpret_cast<const uint4*>(a.q + q_row0 + h * kHeadDim + n * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads (in-order vmcnt)
+  TileCodes x0[4], x1[4];
+  int64_t pg0[4], pg1[4];
+  fetch(tile_begin, x0, pg0);
+
   // ---- query: rotate (R q), scale by softmax_scale * log2(e), stage in LDS in natural order
   const LaneFwht lf = lane_fwht(a.rot, n);
-  for (int h0 = 0; h0 < g; h0 += 4) {
-    const int h = h0 + G;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int h = 4 * r + G;
+    if (4 * r >= g) break;
     float x[8];
-    const uint4 w = (h < g) ? *reinterpret_cast<const uint4*>(a.q + q_row0 + h * kHeadDim + n * 8) : make_uint4(0, 0, 0, 0);
-    bf16x8_to_f32(w, x);
+    bf16x8_to_f32(qw[r], x);
     int pos = n;
     if (!a.q_prerotated) {
       fwht_row16_planned(x, a.rot, lf);
@@ -201,7 +276,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       for (int k = 0; k < 8; ++k) qs[h][8 * pos + k] = x[k] * a.qk_scale_log2;
     }
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- query as 21-bit fixed point x = rint(q' 2^E), |x| <= 2^20, in three int8 limbs
   float qv[32];
@@ -248,76 +323,69 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   const float inv_scale = ldexpf(1.0f, -E);     // q' = x 2^-E
   const float sum_q = static_cast<float>(sx);   // sum of x over the 128 channels
 
-  // ---- walk the split's tiles two at a time
-  const int tile_begin = p_begin * tiles_per_page;
-  const int tile_end = min(p_end * tiles_per_page, (len + 15) / 16);
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
-
-  v4f acc[8];
+  auto step = [&](const TileCodes (&c)[4], const int64_t (&pg)[4], int tile) {
+    const bool full = (tile + 3 < full_end) && pg[0] >= 0 && pg[1] >= 0 && pg[2] >= 0 && pg[3] >= 0;
+    // stage the scale/zero blocks
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;   // running maximum of head n (log2 units), equal in the 4 lanes of head n
-  float l_part = 0.f;      // this lane's share of sum p (head n)
-  float z_part = 0.f;      // this lane's share of sum p (z - B delta) (head n)
+    for (int u = 0; u < 4; ++u) reinterpret_cast<float*>(szs[u])[lane] = c[u].sz;
+    wave_lds_sync();
 
-  auto page_of = [&](int tile) -> int64_t {
-    const int32_t p = bt[tile / tiles_per_page];
-    return (p >= 0 && p < a.num_pages) ? p : -1;
-  };
-  // Loads of tiles (t, t+1) into (x, y); a missing or invalid tile re-reads a valid one and is
-  // masked out through its page flag.
-  auto fetch = [&](int t, TileLoad& x, TileLoad& y, int64_t& px, int64_t& py) {
-    px = page_of(t);
-    py = (t + 1 < tile_end) ? page_of(t + 1) : -1;
-    const int64_t sx = px < 0 ? 0 : px;
-    x = load_tile<BITS>(a, sx, t % tiles_per_page, kvh, G, n);
-    y = load_tile<BITS>(a, py < 0 ? sx : py, (t + 1) % tiles_per_page, kvh, G, n);
-  };
-
-  auto step = [&](const TileLoad& ca, const TileLoad& cb, int64_t pa, int64_t pb, int tile) {
-    const bool a_ok = pa >= 0;
-    const bool b_ok = (tile + 1 < tile_end) && pb >= 0;
-    // QK^T for both tiles: exact int32 dot products of the codes with the fixed-point query
-    v4i sa = v4i{0, 0, 0, 0}, sb = v4i{0, 0, 0, 0};
-    const v4i ka0 = k_operand<BITS>(ca.k, 0), ka1 = k_operand<BITS>(ca.k, 1);
-    const v4i kb0 = k_operand<BITS>(cb.k, 0), kb1 = k_operand<BITS>(cb.k, 1);
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka0, L0[0], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb0, L0[0], sb, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1, L0[1], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb1, L0[1], sb, 0, 0, 0);
-    sa = sa << 7;
-    sb = sb << 7;
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka0, L1[0], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb0, L1[0], sb, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1, L1[1], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb1, L1[1], sb, 0, 0, 0);
-    sa = sa << 7;
-    sb = sb << 7;
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka0, L2[0], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb0, L2[0], sb, 0, 0, 0);
-    sa = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka1, L2[1], sa, 0, 0, 0);
-    sb = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb1, L2[1], sb, 0, 0, 0);
-
-    // scores (log2 units) of head n, tokens 4G+i of tile a (s[i]) and tile b (s[4+i])
-    const int tok_a = tile * 16 + 4 * G, tok_b = tok_a + 16;
-    const float kd[8] = {ca.ksz01.x, ca.ksz01.z, ca.ksz23.x, ca.ksz23.z, cb.ksz01.x, cb.ksz01.z, cb.ksz23.x, cb.ksz23.z};
-    const float kz[8] = {ca.ksz01.y, ca.ksz01.w, ca.ksz23.y, ca.ksz23.w, cb.ksz01.y, cb.ksz01.w, cb.ksz23.y, cb.ksz23.w};
-    const float vd[8] = {ca.vsz01.x, ca.vsz01.z, ca.vsz23.x, ca.vsz23.z, cb.vsz01.x, cb.vsz01.z, cb.vsz23.x, cb.vsz23.z};
-    const float vz[8] = {ca.vsz01.y, ca.vsz01.w, ca.vsz23.y, ca.vsz23.w, cb.vsz01.y, cb.vsz01.w, cb.vsz23.y, cb.vsz23.w};
-    float s[8];
-    bool ok[8];
+    // QK^T for the four tiles: exact int32 dot products of the codes with the fixed-point query
+    v4i sc[4];
+    v4i kop[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int acc_i = i < 4 ? sa[i] : sb[i - 4];
-      ok[i] = (i < 4 ? (a_ok && tok_a + i < len) : (b_ok && tok_b + i - 4 < len));
-      const float sc = inv_scale * __builtin_fmaf(kd[i], static_cast<float>(acc_i), kz[i] * sum_q);
-      s[i] = ok[i] ? sc : kNegInf;
+    for (int u = 0; u < 4; ++u) {
+      sc[u] = v4i{0, 0, 0, 0};
+      kop[u][0] = k_operand<BITS>(c[u].k, 0);
+      kop[u][1] = k_operand<BITS>(c[u].k, 1);
     }
-    float mt = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L0[0], sc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L0[1], sc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = sc[u] << 7;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L1[0], sc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L1[1], sc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = sc[u] << 7;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L2[0], sc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L2[1], sc[u], 0, 0, 0);
+
+    // raw scores t = delta (q~.c) + z sum(q~), in units of 2^E * log2; tokens 4G+i of tile u
+    float sr[16], vd[16], vzz[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 k01 = szs[u][2 * G], k23 = szs[u][2 * G + 1];
+      const float4 v01 = szs[u][8 + 2 * G], v23 = szs[u][8 + 2 * G + 1];
+      const float kd[4] = {k01.x, k01.z, k23.x, k23.z};
+      const float kz[4] = {k01.y, k01.w, k23.y, k23.w};
+      const float vdd[4] = {v01.x, v01.z, v23.x, v23.z};
+      const float vz[4] = {v01.y, v01.w, v23.y, v23.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = __builtin_fmaf(kd[i], static_cast<float>(sc[u][i]), kz[i] * sum_q);
+        if (!full) {
+          const bool ok = pg[u] >= 0 && (tile + u) * 16 + 4 * G + i < len;
+          t = ok ? t : kNegInf;
+        }
+        sr[4 * u + i] = t;
+        vd[4 * u + i] = vdd[i];
+        vzz[4 * u + i] = __builtin_fmaf(-VBias<BITS>::value, vdd[i], vz[i]);
+      }
+    }
+    float mt = sr[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sr[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (__any(mt > m_run + kLazyRescale)) {
-      const float m_new = (mt > m_run + kLazyRescale) ? mt : m_run;
+    mt *= inv_scale;  // log2 units
+    if (__any(mt > m_run + lazy)) {
+      const float m_new = (mt > m_run + lazy) ? mt : m_run;
       const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
@@ -330,40 +398,50 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         for (int m = 0; m < 8; ++m) acc[m][i] *= ai;
       }
     }
-    float w[8];
+    const float m_ref = (m_run == kNegInf) ? 0.f : m_run;  // only a step with no valid token leaves -inf
+    float w[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = ok[i] ? __builtin_amdgcn_exp2f(s[i] - m_run) : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      // p = 2^(t 2^-E - m); invalid tokens have t = -inf and so p = 0
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(inv_scale, sr[i], -m_ref));
       l_part += p;
-      z_part = __builtin_fmaf(p, ok[i] ? __builtin_fmaf(-VBias<BITS>::value, vd[i], vz[i]) : 0.f, z_part);
-      w[i] = ok[i] ? p * vd[i] : 0.f;
+      if (full) {
+        z_part = __builtin_fmaf(p, vzz[i], z_part);
+        w[i] = p * vd[i];
+      } else {  // rows past the end may hold anything, even NaN: select, do not multiply
+        z_part = __builtin_fmaf(p, (sr[i] == kNegInf) ? 0.f : vzz[i], z_part);
+        w[i] = (sr[i] == kNegInf) ? 0.f : p * vd[i];
+      }
     }
-    uint32_t h01a, h23a, l01a, l23a, h01b, h23b, l01b, l23b;
-    split_bf16({w[0], w[1], w[2], w[3]}, h01a, h23a, l01a, l23a);
-    split_bf16({w[4], w[5], w[6], w[7]}, h01b, h23b, l01b, l23b);
-    const v8bf p_hi = as_bf(v4u{h01a, h23a, h01b, h23b});
-    const v8bf p_lo = as_bf(v4u{l01a, l23a, l01b, l23b});
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const uint32_t na = v_bf16_low_bytes<BITS>(ca.v, m);
-      const uint32_t nb = v_bf16_low_bytes<BITS>(cb.v, m);
-      const v8bf vb = as_bf(v4u{bias_bf16_lo<BITS>(na), bias_bf16_hi<BITS>(na), bias_bf16_lo<BITS>(nb),
-                                bias_bf16_hi<BITS>(nb)});
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc[m], 0, 0, 0);
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc[m], 0, 0, 0);
+    for (int hpair = 0; hpair < 2; ++hpair) {
+      const int u0 = 2 * hpair, u1 = u0 + 1;
+      uint32_t h01a, h23a, l01a, l23a, h01b, h23b, l01b, l23b;
+      split_bf16({w[4 * u0], w[4 * u0 + 1], w[4 * u0 + 2], w[4 * u0 + 3]}, h01a, h23a, l01a, l23a);
+      split_bf16({w[4 * u1], w[4 * u1 + 1], w[4 * u1 + 2], w[4 * u1 + 3]}, h01b, h23b, l01b, l23b);
+      const v8bf p_hi = as_bf(v4u{h01a, h23a, h01b, h23b});
+      const v8bf p_lo = as_bf(v4u{l01a, l23a, l01b, l23b});
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const uint32_t na = v_bf16_low_bytes<BITS>(c[u0].v, m);
+        const uint32_t nb = v_bf16_low_bytes<BITS>(c[u1].v, m);
+        const v8bf vb = as_bf(v4u{bias_bf16_lo<BITS>(na), bias_bf16_hi<BITS>(na), bias_bf16_lo<BITS>(nb),
+                                  bias_bf16_hi<BITS>(nb)});
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc[m], 0, 0, 0);
+      }
     }
+    wave_lds_sync();  // the scale/zero block is rewritten by the next step
   };
 
-  // Double-buffered walk: buffer 0 holds tiles (t, t+1) while tiles (t+2, t+3) load into buffer 1.
-  TileLoad x0, y0, x1, y1;
-  int64_t px0, py0, px1 = -1, py1 = -1;
-  fetch(tile_begin, x0, y0, px0, py0);
-  for (int tile = tile_begin; tile < tile_end; tile += 4) {
-    if (tile + 2 < tile_end) fetch(tile + 2, x1, y1, px1, py1);
-    step(x0, y0, px0, py0, tile);
-    if (tile + 2 >= tile_end) break;
-    if (tile + 4 < tile_end) fetch(tile + 4, x0, y0, px0, py0);
-    step(x1, y1, px1, py1, tile + 2);
+  // Double-buffered walk: buffer 0 holds tiles t..t+3 while t+4..t+7 load into buffer 1.
+  for (int tile = tile_begin;; tile += 8) {
+    fetch(tile + 4, x1, pg1);
+    step(x0, pg0, tile);
+    if (tile + 4 >= tile_end) break;
+    fetch(tile + 8, x0, pg0);
+    step(x1, pg1, tile + 4);
+    if (tile + 8 >= tile_end) break;
   }
 
   // ---- finish: totals of head n, then moved to the accumulator rows (heads 4G+i)
@@ -394,17 +472,73 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
     }
-  } else {
-    const int64_t base = (static_cast<int64_t>(split) * a.batch + b) * a.num_q_heads + static_cast<int64_t>(kvh) * g;
+    return;
+  }
+
+  // Split: publish this split's partial (un-normalised accumulator with its zero term, running
+  // maximum and sum) for the merge kernel.
+  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int64_t head0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * G + i;
-      if (h < g) {
-        float4* dst = reinterpret_cast<float4*>(a.ws_acc + (base + h) * kHeadDim + 8 * n);
-        dst[0] = make_float4(acc[0][i] + zrow[i], acc[1][i] + zrow[i], acc[2][i] + zrow[i], acc[3][i] + zrow[i]);
-        dst[1] = make_float4(acc[4][i] + zrow[i], acc[5][i] + zrow[i], acc[6][i] + zrow[i], acc[7][i] + zrow[i]);
-        if (n == 0) reinterpret_cast<float2*>(a.ws_ml)[base + h] = make_float2(mrow[i], lrow[i]);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * G + i;
+    if (h < g) {
+      const int64_t row = split * pairs + head0 + h;
+      float4* dst = reinterpret_cast<float4*>(a.ws_acc + row * kHeadDim + 8 * n);
+      dst[0] = make_float4(acc[0][i] + zrow[i], acc[1][i] + zrow[i], acc[2][i] + zrow[i], acc[3][i] + zrow[i]);
+      dst[1] = make_float4(acc[4][i] + zrow[i], acc[5][i] + zrow[i], acc[6][i] + zrow[i], acc[7][i] + zrow[i]);
+      if (n == 0) reinterpret_cast<float2*>(a.ws_ml)[row] = make_float2(mrow[i], lrow[i]);
+    }
+  }
+}
+
+// Log-sum-exp merge of the split partials of one (sequence, KV head): row group G merges heads G
+// and G + 4, lane n channels 8n..8n+7; the maxima are reduced first, then every split's partial is
+// loaded with independent (unrolled) loads, combined, rotated back and stored.
+__global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int G = lane >> 4;
+  const int n = lane & 15;
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = a.num_q_heads / a.num_kv_heads;
+  const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
+  const int n_pages = (len + a.page_size - 1) / a.page_size;
+  const int n_used = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  const LaneFwht lf = lane_fwht(a.rot, n);
+  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int64_t head0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g;
+  const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
+  for (int h0 = 0; h0 < g; h0 += 4) {
+    const int h = h0 + G;
+    const bool live = h < g && n_used > 0;
+    const int64_t row0 = head0 + (live ? h : 0);
+    const int nu = live ? n_used : 0;
+    float mo = kNegInf;
+    for (int sp = n; sp < nu; sp += 16) mo = fmaxf(mo, ml_all[sp * pairs + row0].x);
+    mo = row16_max(mo);
+    float lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int sp = 0; sp < nu; ++sp) {
+      const int64_t row = sp * pairs + row0;
+      const float2 ml = ml_all[row];
+      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + row * kHeadDim + 8 * n);
+      const float4 x0v = src[0], x1v = src[1];
+      const float f = __builtin_amdgcn_exp2f(ml.x - mo);
+      lsum = __builtin_fmaf(ml.y, f, lsum);
+      o[0] = __builtin_fmaf(x0v.x, f, o[0]); o[1] = __builtin_fmaf(x0v.y, f, o[1]);
+      o[2] = __builtin_fmaf(x0v.z, f, o[2]); o[3] = __builtin_fmaf(x0v.w, f, o[3]);
+      o[4] = __builtin_fmaf(x1v.x, f, o[4]); o[5] = __builtin_fmaf(x1v.y, f, o[5]);
+      o[6] = __builtin_fmaf(x1v.z, f, o[6]); o[7] = __builtin_fmaf(x1v.w, f, o[7]);
+    }
+    const float inv_l = (nu > 0) ? 1.0f / lsum : 0.f;  // an empty sequence yields zeros
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] *= inv_l;
+    fwht_row16_planned(o, a.rot, lf);
+    if (h < g) {
+      float4* dst = reinterpret_cast<float4*>(a.out + (head0 + h) * kHeadDim + 8 * lf.pos);
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
     }
   }
 }
@@ -414,11 +548,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads),
                   static_cast<unsigned>(a.batch));
+  const bool ps16 = a.page_size == 16;
   if (a.bits == 4) {
-    hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<4, false>), grid, dim3(64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(decode_mfma_kernel<2>, grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false>), grid, dim3(64), 0, stream, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const dim3 mgrid(static_cast<unsigned>(a.num_kv_heads), static_cast<unsigned>(a.batch));
+  hipLaunchKernelGGL(decode_merge_splits_kernel, mgrid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -167,6 +167,11 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_c
                                                        page_size, pages_per_split))
 
 
+def decode_workspace(nbytes: int, device) -> torch.Tensor:
+    """A decode workspace of ``nbytes``: zero-filled, as the library requires before first use."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
                            context_lens: torch.Tensor, max_context_len: int, hadamard_block: int,
                            softmax_scale: float = 0.0, q_prerotated: int = 0, out: torch.Tensor | None = None,
@@ -187,7 +192,7 @@ def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: to
         raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(need, q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().kvq_paged_decode_attention(
