@@ -25,9 +25,17 @@
 // Online softmax in base 2 with a lazy maximum: the accumulators are rescaled only when a tile's
 // maximum exceeds the running one by more than 8 (so p <= 2^8 in between).
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq_device.h"
 #include "kvq_launch.h"
+
+#ifndef KVQ_DECODE_STEP_TILES
+#define KVQ_DECODE_STEP_TILES 2   // 16-token tiles per step (2 or 4)
+#endif
+#ifndef KVQ_DECODE_MIN_WAVES
+#define KVQ_DECODE_MIN_WAVES 2    // waves per SIMD the register allocation must allow
+#endif
 
 namespace kvq {
 namespace {
@@ -45,6 +53,15 @@ constexpr float kNegInf = -__builtin_inff();
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 __device__ __forceinline__ int32_t ro_load(const int32_t* p, int64_t i) {
   return ((const_i32*)(p))[i];
+}
+
+// Maximum over the four 16-lane rows (lanes n, n+16, n+32, n+48), in every lane: gfx950's row
+// swaps exchange rows 0<->1, 2<->3 and then the two halves, without going through LDS.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Orders this wave's LDS writes before its later LDS reads (one-wave workgroups: no s_barrier,
@@ -125,17 +142,26 @@ __device__ __forceinline__ v4i k_operand(const uint4 w, int j) {
 }
 
 // Channel 8n + m of the four tokens of this lane group as bf16 low bytes 0x80 | c << shift
-// (shift 3 for INT4, 5 for INT2), one token per byte.
+// (shift 3 for INT4, 5 for INT2), one token per byte. `c80` holds 0x80808080 in a VGPR, so each
+// byte costs two VOP3 operations (shift/mask + or) instead of three.
 template <int BITS>
-__device__ __forceinline__ uint32_t v_bf16_low_bytes(const uint4 w, int m) {
+__device__ __forceinline__ uint32_t v_bf16_low_bytes(const uint4 w, int m, uint32_t c80) {
   if constexpr (BITS == 4) {
     const uint32_t d = (m >> 1) == 0 ? w.x : (m >> 1) == 1 ? w.y : (m >> 1) == 2 ? w.z : w.w;
-    return (((m & 1) ? (d >> 1) : (d << 3)) & 0x78787878u) | 0x80808080u;
+    if (m & 1) return ((d >> 1) & 0x78787878u) | c80;  // high nibble: bits 4..7 -> 3..6
+    return ((d & 0x0F0F0F0Fu) << 3) | c80;              // low nibble: bits 0..3 -> 3..6
   } else {
     const uint32_t d = (m >> 2) ? w.y : w.x;
     const int sh = 2 * (m & 3);  // crumb position; target bits 5..6
-    return (((sh <= 5) ? (d << (5 - sh)) : (d >> (sh - 5))) & 0x60606060u) | 0x80808080u;
+    if (sh == 0) return ((d & 0x03030303u) << 5) | c80;
+    return (((sh <= 5) ? (d << (5 - sh)) : (d >> (sh - 5))) & 0x60606060u) | c80;
   }
+}
+
+// A constant kept in a VGPR (the empty register-only asm makes it opaque to the compiler).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // One 16-token tile as this lane loads it: K codes of token n (channels 32G..32G+31), V codes of
@@ -160,13 +186,14 @@ struct LaneOffsets {
   const float* sz;     // this lane's scale/zero array (K for lanes 0..31, V for 32..63) + lane offset
 };
 
+// Loads one tile whose first token row (in the [page][head][token] row numbering shared by the
+// code and scale/zero arrays) is row0.
 template <int BITS>
-__device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t page, int sub, int kvh,
-                                               const LaneOffsets& lo) {
-  constexpr int kRow = kHeadDim * BITS / 8;
-  const int64_t row0 = (page * a.num_kv_heads + kvh) * a.page_size + 16 * sub;  // first token row
-  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + row0 * kRow, 16 * kRow);
-  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + row0 * kRow, 16 * kRow);
+__device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t row0, const LaneOffsets& lo) {
+  constexpr int kRowShift = (BITS == 4) ? 6 : 5;  // log2(bytes per token row)
+  const int64_t off = row0 << kRowShift;
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + off, 16 << kRowShift);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + off, 16 << kRowShift);
   TileCodes t;
   if constexpr (BITS == 4) {
     t.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k, 0, 0));
@@ -181,10 +208,10 @@ __device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t page
   return t;
 }
 
-template <int BITS, bool PS16>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
+template <int BITS, bool PS16, int NT>
+__global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
   __shared__ float qs[8][kHeadDim];
-  __shared__ float4 szs[4][16];  // scale/zero of the four tiles in flight: [tile][K floats 0..31 | V floats 32..63]
+  __shared__ float4 szs[2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
 
   const int lane = threadIdx.x;
   const int G = lane >> 4;
@@ -212,7 +239,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     return;
   }
 
-  // ---- walk the split's tiles, four per step, the next four loading meanwhile
+  // ---- walk the split's tiles, NT per step, the next two steps loading meanwhile
   const int tile_begin = p_begin * tiles_per_page;
   const int tile_end = min(p_end * tiles_per_page, (len + 15) / 16);
   const int full_end = min(tile_end, len / 16);  // tiles before this one are entirely valid
@@ -234,14 +261,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   lo.v = (BITS == 4) ? (G * 4 * (kHeadDim / 2) + 16 * n) : (G * 4 * (kHeadDim / 4) + 8 * n);
   lo.sz = (lane < 32) ? a.k_sz + lane : a.v_sz + (lane - 32);
   const int last_tile = tile_end - 1;
-  auto fetch = [&](int t, TileCodes (&x)[4], int64_t (&pg)[4]) {
+  const int64_t page_rows = static_cast<int64_t>(a.num_kv_heads) * ps;  // token rows per page (all heads)
+  const int64_t head_rows = static_cast<int64_t>(kvh) * ps;
+  auto fetch = [&](int t, TileCodes (&x)[NT], int64_t (&pg)[NT]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NT; ++u) {
       const int tt = min(t + u, last_tile);
       const int32_t p = ro_load(bt, PS16 ? tt : tt / tiles_per_page);
       const bool ok = (p >= 0 && p < a.num_pages);
       pg[u] = (ok && t + u <= last_tile) ? p : -1;
-      x[u] = load_tile<BITS>(a, ok ? p : 0, PS16 ? 0 : tt % tiles_per_page, kvh, lo);
+      const int64_t row0 = (ok ? p : 0) * page_rows + head_rows + (PS16 ? 0 : 16 * (tt % tiles_per_page));
+      x[u] = load_tile<BITS>(a, row0, lo);
     }
   };
 
@@ -254,9 +284,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     qw[r] = *reinterpret_cast<const uint4*>(a.q + q_row0 + h * kHeadDim + n * 8);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads (in-order vmcnt)
-  TileCodes x0[4], x1[4];
-  int64_t pg0[4], pg1[4];
+  TileCodes x0[NT], x1[NT], x2[NT];
+  int64_t pg0[NT], pg1[NT], pg2[NT];
   fetch(tile_begin, x0, pg0);
+  fetch(tile_begin + NT, x1, pg1);
 
   // ---- query: rotate (R q), scale by softmax_scale * log2(e), stage in LDS in natural order
   const LaneFwht lf = lane_fwht(a.rot, n);
@@ -323,45 +354,42 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   const float inv_scale = ldexpf(1.0f, -E);     // q' = x 2^-E
   const float sum_q = static_cast<float>(sx);   // sum of x over the 128 channels
 
-  auto step = [&](const TileCodes (&c)[4], const int64_t (&pg)[4], int tile) {
-    const bool full = (tile + 3 < full_end) && pg[0] >= 0 && pg[1] >= 0 && pg[2] >= 0 && pg[3] >= 0;
-    // stage the scale/zero blocks
-#pragma unroll
-    for (int u = 0; u < 4; ++u) reinterpret_cast<float*>(szs[u])[lane] = c[u].sz;
-    wave_lds_sync();
+  const uint32_t c80 = vgpr_const(0x80808080u);
+  // One step over NT tiles. full (all 16 NT tokens valid, all pages valid) drops every mask.
+  auto step_impl = [&](auto full_tag, const TileCodes (&c)[NT], const int64_t (&pg)[NT], int tile,
+                       const TileCodes (&next)[NT], int buf) {
+    constexpr bool full = decltype(full_tag)::value;
 
-    // QK^T for the four tiles: exact int32 dot products of the codes with the fixed-point query
-    v4i sc[4];
-    v4i kop[4][2];
+    // QK^T for the step's tiles: one exact int32 dot product per query limb (three independent
+    // MFMA chains of depth two), then x = ((s0 * 128) + s1) * 128 + s2 - Horner's rule on the
+    // finished products, every partial sum below 2^31.
+    v4i sc[NT];
+    {
+      v4i s0[NT], s1[NT], s2[NT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sc[u] = v4i{0, 0, 0, 0};
-      kop[u][0] = k_operand<BITS>(c[u].k, 0);
-      kop[u][1] = k_operand<BITS>(c[u].k, 1);
+      for (int u = 0; u < NT; ++u) {
+        const v4i k0 = k_operand<BITS>(c[u].k, 0);
+        s0[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L0[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+        s1[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L1[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+        s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L2[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const v4i k1 = k_operand<BITS>(c[u].k, 1);
+        s0[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L0[1], s0[u], 0, 0, 0);
+        s1[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L1[1], s1[u], 0, 0, 0);
+        s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L2[1], s2[u], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < NT; ++u) sc[u] = (((s0[u] << 7) + s1[u]) << 7) + s2[u];
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L0[0], sc[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L0[1], sc[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = sc[u] << 7;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L1[0], sc[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L1[1], sc[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = sc[u] << 7;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][0], L2[0], sc[u], 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kop[u][1], L2[1], sc[u], 0, 0, 0);
 
     // raw scores t = delta (q~.c) + z sum(q~), in units of 2^E * log2; tokens 4G+i of tile u
-    float sr[16], vd[16], vzz[16];
+    float sr[4 * NT], vd[4 * NT], vzz[4 * NT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 k01 = szs[u][2 * G], k23 = szs[u][2 * G + 1];
-      const float4 v01 = szs[u][8 + 2 * G], v23 = szs[u][8 + 2 * G + 1];
+    for (int u = 0; u < NT; ++u) {
+      const float4 k01 = szs[buf][u][2 * G], k23 = szs[buf][u][2 * G + 1];
+      const float4 v01 = szs[buf][u][8 + 2 * G], v23 = szs[buf][u][8 + 2 * G + 1];
       const float kd[4] = {k01.x, k01.z, k23.x, k23.z};
       const float kz[4] = {k01.y, k01.w, k23.y, k23.w};
       const float vdd[4] = {v01.x, v01.z, v23.x, v23.z};
@@ -369,7 +397,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float t = __builtin_fmaf(kd[i], static_cast<float>(sc[u][i]), kz[i] * sum_q);
-        if (!full) {
+        if constexpr (!full) {
           const bool ok = pg[u] >= 0 && (tile + u) * 16 + 4 * G + i < len;
           t = ok ? t : kNegInf;
         }
@@ -380,9 +408,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
     float mt = sr[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sr[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    for (int i = 1; i < 4 * NT; ++i) mt = fmaxf(mt, sr[i]);
+    mt = max_over_rows(mt);
     mt *= inv_scale;  // log2 units
     if (__any(mt > m_run + lazy)) {
       const float m_new = (mt > m_run + lazy) ? mt : m_run;
@@ -399,13 +426,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       }
     }
     const float m_ref = (m_run == kNegInf) ? 0.f : m_run;  // only a step with no valid token leaves -inf
-    float w[16];
+    float w[4 * NT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4 * NT; ++i) {
       // p = 2^(t 2^-E - m); invalid tokens have t = -inf and so p = 0
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(inv_scale, sr[i], -m_ref));
       l_part += p;
-      if (full) {
+      if constexpr (full) {
         z_part = __builtin_fmaf(p, vzz[i], z_part);
         w[i] = p * vd[i];
       } else {  // rows past the end may hold anything, even NaN: select, do not multiply
@@ -414,7 +441,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int hpair = 0; hpair < 2; ++hpair) {
+    for (int hpair = 0; hpair < NT / 2; ++hpair) {
       const int u0 = 2 * hpair, u1 = u0 + 1;
       uint32_t h01a, h23a, l01a, l23a, h01b, h23b, l01b, l23b;
       split_bf16({w[4 * u0], w[4 * u0 + 1], w[4 * u0 + 2], w[4 * u0 + 3]}, h01a, h23a, l01a, l23a);
@@ -423,25 +450,56 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
       const v8bf p_lo = as_bf(v4u{l01a, l23a, l01b, l23b});
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const uint32_t na = v_bf16_low_bytes<BITS>(c[u0].v, m);
-        const uint32_t nb = v_bf16_low_bytes<BITS>(c[u1].v, m);
+        const uint32_t na = v_bf16_low_bytes<BITS>(c[u0].v, m, c80);
+        const uint32_t nb = v_bf16_low_bytes<BITS>(c[u1].v, m, c80);
         const v8bf vb = as_bf(v4u{bias_bf16_lo<BITS>(na), bias_bf16_hi<BITS>(na), bias_bf16_lo<BITS>(nb),
                                   bias_bf16_hi<BITS>(nb)});
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc[m], 0, 0, 0);
       }
     }
-    wave_lds_sync();  // the scale/zero block is rewritten by the next step
+    // stage the next step's scale/zero blocks (loaded two steps ago) in the other buffer
+#pragma unroll
+    for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[buf ^ 1][u])[lane] = next[u].sz;
+    wave_lds_sync();
+  };
+  auto step = [&](const TileCodes (&c)[NT], const int64_t (&pg)[NT], int tile, const TileCodes (&next)[NT],
+                  int buf) {
+    bool pages_ok = true;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) pages_ok = pages_ok && pg[u] >= 0;
+    if ((tile + NT - 1 < full_end) && pages_ok) {
+      step_impl(std::true_type{}, c, pg, tile, next, buf);
+    } else {
+      step_impl(std::false_type{}, c, pg, tile, next, buf);
+    }
   };
 
-  // Double-buffered walk: buffer 0 holds tiles t..t+3 while t+4..t+7 load into buffer 1.
-  for (int tile = tile_begin;; tile += 8) {
-    fetch(tile + 4, x1, pg1);
-    step(x0, pg0, tile);
-    if (tile + 4 >= tile_end) break;
-    fetch(tile + 8, x0, pg0);
-    step(x1, pg1, tile + 4);
-    if (tile + 8 >= tile_end) break;
+  // Triple-buffered walk: while the tiles of one buffer are processed, the next two steps'
+  // tiles are already loading (about two steps of latency covered).
+  // Step k reads scale/zero buffer k & 1; the six-step cycle keeps the parity aligned.
+#pragma unroll
+  for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[0][u])[lane] = x0[u].sz;
+  wave_lds_sync();
+  for (int tile = tile_begin;; tile += 6 * NT) {
+    fetch(tile + 2 * NT, x2, pg2);
+    step(x0, pg0, tile, x1, 0);
+    if (tile + NT >= tile_end) break;
+    fetch(tile + 3 * NT, x0, pg0);
+    step(x1, pg1, tile + NT, x2, 1);
+    if (tile + 2 * NT >= tile_end) break;
+    fetch(tile + 4 * NT, x1, pg1);
+    step(x2, pg2, tile + 2 * NT, x0, 0);
+    if (tile + 3 * NT >= tile_end) break;
+    fetch(tile + 5 * NT, x2, pg2);
+    step(x0, pg0, tile + 3 * NT, x1, 1);
+    if (tile + 4 * NT >= tile_end) break;
+    fetch(tile + 6 * NT, x0, pg0);
+    step(x1, pg1, tile + 4 * NT, x2, 0);
+    if (tile + 5 * NT >= tile_end) break;
+    fetch(tile + 7 * NT, x1, pg1);
+    step(x2, pg2, tile + 5 * NT, x0, 1);
+    if (tile + 6 * NT >= tile_end) break;
   }
 
   // ---- finish: totals of head n, then moved to the accumulator rows (heads 4G+i)
@@ -492,54 +550,76 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
   }
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, KV head): row group G merges heads G
-// and G + 4, lane n channels 8n..8n+7; the maxima are reduced first, then every split's partial is
-// loaded with independent (unrolled) loads, combined, rotated back and stored.
+// Log-sum-exp merge of the split partials of one (sequence, query head) per wave. Row group G
+// takes splits G, G + 4, G + 8, ...; lane n holds channels 8n..8n+7. Eight splits per group are
+// loaded with independent loads before any is combined, so 32 splits cost one memory round trip.
+// The four groups' running (max, sum, vector) are then combined across rows, rotated back and
+// stored by row group 0.
+__device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], int xor_mask) {
+  const float m2 = __shfl_xor(m, xor_mask);
+  const float l2 = __shfl_xor(l, xor_mask);
+  const float mn = fmaxf(m, m2);
+  const float fa = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+  const float fb = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+  l = l * fa + l2 * fb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = o[i] * fa + __shfl_xor(o[i], xor_mask) * fb;
+  m = mn;
+}
+
 __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int g = a.num_q_heads / a.num_kv_heads;
+  const int64_t pair = blockIdx.x;  // b * num_q_heads + h
+  const int b = static_cast<int>(pair / a.num_q_heads);
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + a.page_size - 1) / a.page_size;
-  const int n_used = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  const int nu = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
   const LaneFwht lf = lane_fwht(a.rot, n);
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
-  const int64_t head0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g;
   const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
-  for (int h0 = 0; h0 < g; h0 += 4) {
-    const int h = h0 + G;
-    const bool live = h < g && n_used > 0;
-    const int64_t row0 = head0 + (live ? h : 0);
-    const int nu = live ? n_used : 0;
-    float mo = kNegInf;
-    for (int sp = n; sp < nu; sp += 16) mo = fmaxf(mo, ml_all[sp * pairs + row0].x);
-    mo = row16_max(mo);
-    float lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int sp = 0; sp < nu; ++sp) {
-      const int64_t row = sp * pairs + row0;
-      const float2 ml = ml_all[row];
-      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + row * kHeadDim + 8 * n);
-      const float4 x0v = src[0], x1v = src[1];
-      const float f = __builtin_amdgcn_exp2f(ml.x - mo);
-      lsum = __builtin_fmaf(ml.y, f, lsum);
-      o[0] = __builtin_fmaf(x0v.x, f, o[0]); o[1] = __builtin_fmaf(x0v.y, f, o[1]);
-      o[2] = __builtin_fmaf(x0v.z, f, o[2]); o[3] = __builtin_fmaf(x0v.w, f, o[3]);
-      o[4] = __builtin_fmaf(x1v.x, f, o[4]); o[5] = __builtin_fmaf(x1v.y, f, o[5]);
-      o[6] = __builtin_fmaf(x1v.z, f, o[6]); o[7] = __builtin_fmaf(x1v.w, f, o[7]);
-    }
-    const float inv_l = (nu > 0) ? 1.0f / lsum : 0.f;  // an empty sequence yields zeros
+  float mo = kNegInf, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nu; s0 += 32) {
+    float2 ml[8];
+    float4 xa[8], xb[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) o[m] *= inv_l;
-    fwht_row16_planned(o, a.rot, lf);
-    if (h < g) {
-      float4* dst = reinterpret_cast<float4*>(a.out + (head0 + h) * kHeadDim + 8 * lf.pos);
-      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    for (int j = 0; j < 8; ++j) {
+      const int sp = min(s0 + G + 4 * j, nu - 1);  // past the end: re-read the last split, weight 0
+      const int64_t row = sp * pairs + pair;
+      ml[j] = ml_all[row];
+      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + row * kHeadDim + 8 * n);
+      xa[j] = src[0];
+      xb[j] = src[1];
     }
+    float mc = mo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mc = fmaxf(mc, (s0 + G + 4 * j < nu) ? ml[j].x : kNegInf);
+    const float r = (mo == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mo - mc);
+    lsum *= r;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[m] *= r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = (s0 + G + 4 * j < nu) ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
+      lsum = __builtin_fmaf(ml[j].y, f, lsum);
+      o[0] = __builtin_fmaf(xa[j].x, f, o[0]); o[1] = __builtin_fmaf(xa[j].y, f, o[1]);
+      o[2] = __builtin_fmaf(xa[j].z, f, o[2]); o[3] = __builtin_fmaf(xa[j].w, f, o[3]);
+      o[4] = __builtin_fmaf(xb[j].x, f, o[4]); o[5] = __builtin_fmaf(xb[j].y, f, o[5]);
+      o[6] = __builtin_fmaf(xb[j].z, f, o[6]); o[7] = __builtin_fmaf(xb[j].w, f, o[7]);
+    }
+    mo = mc;
+  }
+  lse_combine(mo, lsum, o, 16);
+  lse_combine(mo, lsum, o, 32);
+  const float inv_l = (nu > 0) ? 1.0f / lsum : 0.f;  // an empty sequence yields zeros
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] *= inv_l;
+  fwht_row16_planned(o, a.rot, lf);
+  if (G == 0) {
+    float4* dst = reinterpret_cast<float4*>(a.out + pair * kHeadDim + 8 * lf.pos);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -549,17 +629,18 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads),
                   static_cast<unsigned>(a.batch));
   const bool ps16 = a.page_size == 16;
+  constexpr int kNT = KVQ_DECODE_STEP_TILES;
   if (a.bits == 4) {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<4, false>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, kNT>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, kNT>), grid, dim3(64), 0, stream, a);
   } else {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<2, false>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, kNT>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, kNT>), grid, dim3(64), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  const dim3 mgrid(static_cast<unsigned>(a.num_kv_heads), static_cast<unsigned>(a.batch));
-  hipLaunchKernelGGL(decode_merge_splits_kernel, mgrid, dim3(64), 0, stream, a);
+  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  hipLaunchKernelGGL(decode_merge_splits_kernel, dim3(static_cast<unsigned>(pairs)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
