@@ -43,6 +43,12 @@ def parse_args():
     p.add_argument("--workload", default="llama3_8b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-iters", type=int, default=200, help="extra decode-only launches for the decode roofline")
+    p.add_argument("--counters", action="store_true",
+                   help="short program for rocprofv3 --pmc passes: a 256 MiB calibration copy, then --steps steps")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="print the HBM traffic summary of two rocprofv3 --pmc runs of --counters")
+    p.add_argument("--summarize-kernel-stats", metavar="RUN_DIR",
+                   help="print the kernel table of a rocprofv3 --kernel-trace --stats run as markdown")
     return p.parse_args()
 
 
@@ -63,11 +69,141 @@ def decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size
     return toks * num_kv_heads * per_token_head + pages * 4 + b * num_q_heads * d * (2 + 4) + b * 4
 
 
+# ----------------------------------------------------------------------------- HBM traffic counters
+#
+# rocprofv3's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) do not count every byte the same way
+# (FETCH_SIZE counts a 128-byte read as one 64-byte request), so each is scaled by the ratio it
+# shows on a plain 256 MiB device copy in the same run. The traffic recorded for a kernel is tied
+# to the sources it was built from: once they change, the stored figure no longer applies.
+
+CSRC = os.path.join(ROOT, "paged_decode_attention_amd", "csrc")
+KERNEL_SOURCES = {
+    "append_kernel": ["kvq_append.hip", "kvq_device.h", "kvq_launch.h", "../build.py"],
+    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_device.h", "kvq_launch.h", "../build.py"],
+    "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_device.h", "kvq_launch.h", "../build.py"],
+}
+CALIBRATION_BYTES = 256 << 20
+TRAFFIC_TAG = "traffic-json: "
+
+
+def sources_sha256(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+
+
+def stored_traffic(workload: str, kernel: str):
+    """Measured HBM bytes per launch of ``kernel``, or None if absent or taken on other sources."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith(TRAFFIC_TAG):
+                rec = json.loads(line[len(TRAFFIC_TAG):]).get(kernel)
+                if rec and rec["sources_sha256"] == sources_sha256(kernel):
+                    return rec["bytes_per_launch"]
+    return None
+
+
+def _short_kernel_name(name: str) -> str:
+    for k in list(KERNEL_SOURCES) + ["copyBuffer"]:
+        if k in name:
+            return k
+    return name.split("(")[0][-60:]
+
+
+def _counter_rows(run_dir: str, counter: str):
+    """(kernel, grid, value) per dispatch, in dispatch order."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), _short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]),
+                                 float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {run_dir}")
+    return [r[1:] for r in sorted(rows)]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
+    per = {}
+    factors = {}
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(run_dir, counter)
+        # --counters issues its three calibration copies after every set-up copy and before the
+        # steps, which copy nothing: they are the last three copy dispatches of the run
+        cal = [v for k, g, v in rows if k == "copyBuffer"][-3:]
+        factors[counter] = CALIBRATION_BYTES / (1024.0 * float(np.median(cal)))
+        for k, g, v in rows:
+            if k in KERNEL_SOURCES:
+                per.setdefault((k, g), {}).setdefault(counter, []).append(v)
+    lines = ["| kernel | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |",
+             "|---|---|---|---|---|---|---|"]
+    rec = {}
+    for (k, g), cs in sorted(per.items()):
+        fk = float(np.median(cs.get("FETCH_SIZE", [0.0])))
+        wk = float(np.median(cs.get("WRITE_SIZE", [0.0])))
+        rd = fk * 1024 * factors["FETCH_SIZE"]
+        wr = wk * 1024 * factors["WRITE_SIZE"]
+        lines.append(f"| {k} | {g} | {len(cs.get('FETCH_SIZE', []))} | {fk:.1f} | {wk:.1f} | {rd / 1e6:.2f} | "
+                     f"{wr / 1e6:.2f} |")
+        # the record keeps the largest grid of each kernel (the prefill append, the full decode)
+        if k not in rec or g > rec[k]["grid"]:
+            rec[k] = {"grid": g, "bytes_per_launch": int(rd + wr), "read_bytes": int(rd), "write_bytes": int(wr),
+                      "sources_sha256": sources_sha256(k)}
+    head = [f"# HBM traffic per launch, {workload}", "",
+            f"Command (twice, once per counter): `{command}`", "",
+            f"Calibration: a {CALIBRATION_BYTES >> 20} MiB device copy (__amd_rocclr_copyBuffer) in the same run reads "
+            f"FETCH_SIZE x {factors['FETCH_SIZE']:.4f} and writes WRITE_SIZE x {factors['WRITE_SIZE']:.4f} of its true "
+            "size; every kernel's counters are scaled by these factors (median over dispatches).", ""]
+    return "\n".join(head + lines + ["", TRAFFIC_TAG + json.dumps(rec, sort_keys=True), ""])
+
+
+def _clean_kernel_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0][-70:]
+
+
+def summarize_kernel_stats(run_dir: str, command: str) -> str:
+    """The --stats table of a rocprofv3 --kernel-trace run, plus per-grid averages from its trace
+    (the prefill append and the one-token append are the same kernel on different grids)."""
+    import csv
+    with open(os.path.join(run_dir, "run_kernel_stats.csv")) as fh:
+        rows = list(csv.DictReader(fh))
+    out = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+           "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {_clean_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    per = {}
+    with open(os.path.join(run_dir, "run_kernel_trace.csv")) as fh:
+        for r in csv.DictReader(fh):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            key = (_clean_kernel_name(r["Kernel_Name"]), grid)
+            per.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out += ["", "Per grid (from the kernel trace):", "",
+            "| kernel | grid (work-items) | calls | average us | median us |", "|---|---|---|---|---|"]
+    for (k, g), d in sorted(per.items()):
+        out.append(f"| {k} | {g} | {len(d)} | {np.mean(d):.2f} | {np.median(d):.2f} |")
+    return "\n".join(out + [""])
+
+
 def cpu_baseline(shape, k, v, slots, plan, q) -> dict:
     """The CPU oracle, as it stands, on a bounded sample of the same workload."""
     from oracle import kvq_oracle as O
     cores = len(os.sched_getaffinity(0))
-    n_seq = 8
+    n_seq = shape.batch if shape.batch <= 16 else 8
     n_tok = n_seq * shape.context_lens[0]
     cache = O.PagedCache(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.head_dim, shape.bits)
     t0 = time.perf_counter()
@@ -89,6 +225,16 @@ def cpu_baseline(shape, k, v, slots, plan, q) -> dict:
 
 def main():
     args = parse_args()
+    if args.summarize_counters:
+        cmd = (f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run -- python3 bench.py "
+               f"--counters --workload {args.workload} --steps {args.steps} --warmup 0")
+        print(summarize_counters(*args.summarize_counters, args.workload, cmd))
+        return
+    if args.summarize_kernel_stats:
+        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
+               f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
+        print(summarize_kernel_stats(args.summarize_kernel_stats, cmd))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and this build has "
@@ -169,6 +315,18 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
+    if args.counters:
+        # calibration copy of known size, then the steps the counters are read on
+        src = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        print(f"counters run: 3 calibration copies of {CALIBRATION_BYTES} bytes, {args.steps} steps", flush=True)
+        return
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -227,12 +385,16 @@ def main():
     dominant = "rotate_quantize_append_prefill" if pre_avg >= attn_avg else "paged_decode_attention_alone"
     dom_bytes, dom_ms = (b_prefill, pre_avg) if dominant.startswith("rotate") else (b_attn, dec_avg)
     achieved = gbps(dom_bytes, dom_ms)
+    t_app = stored_traffic(shape.name, "append_kernel")
+    t_dec = [stored_traffic(shape.name, k) for k in ("decode_mfma_kernel", "decode_merge_splits_kernel")]
+    t_dec = None if None in t_dec else sum(t_dec)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": dominant,
+                "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": t_app if dominant.startswith("rotate") else t_dec, "kernel": dominant,
                 "bytes_per_launch": dom_bytes}
     roofline_decode = {"bound": "hbm", "achieved": round(gbps(b_attn, dec_avg), 1), "peak": PEAK_HBM_GBPS,
-                       "unit": "GB/s", "frac": round(gbps(b_attn, dec_avg) / PEAK_HBM_GBPS, 4), "traffic": None,
-                       "kernel": "paged_decode_attention", "bytes_per_launch": b_attn}
+                       "unit": "GB/s", "frac": round(gbps(b_attn, dec_avg) / PEAK_HBM_GBPS, 4), "traffic": t_dec,
+                       "kernel": "paged_decode_attention (decode + split merge)", "bytes_per_launch": b_attn}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -34,6 +34,10 @@ notes of the repository):
     A constant vector gets scale 0, zero = min and all-zero codes.
   * Per-token scaling (OScaR): s = RMS of the rotated vector (s = 1 when it is 0),
     u = y / s; the stored scale and zero are scale_u * s and min_u * s.
+    Parity unpinned: the pages name no norm for s, so RMS is a reading that nothing on
+    the pages can confirm. ``token_rms`` itself is pinned to closed forms. The choice
+    barely matters here: any positive s cancels in the codes, and the stored scale and
+    zero change only by float32 rounding.
   * Packing: low bits first (INT4: channel 2j in the low nibble of byte j).
   * Layout (caller-owned arrays, all row-major):
       K codes  [num_pages][kv_heads][page_size][row]               row = D * bits / 8 bytes

@@ -270,6 +270,10 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_l
     int64_t splits = (2048 + items - 1) / items;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (max_pages + 7) / 8));
     pps = (max_pages + splits - 1) / splits;
+    // The matrix-core kernel walks two pages per step: an even split size keeps every split but
+    // the last free of a half-empty step. Rounding down leaves at most a short extra split (the
+    // page of the newest token) rather than a half step in every split.
+    if (splits > 1 && pps > 8) pps &= ~int64_t{1};
   }
   pps = std::max<int64_t>(1, std::min<int64_t>(pps, max_pages));
   p.pages_per_split = static_cast<int32_t>(pps);

@@ -204,6 +204,24 @@ def pin_quantizer_degenerate():
     assert np.all(c2 == 0) and s2[0] == 0 and z2[0] == 0
 
 
+def pin_token_rms_closed_form():
+    """The per-token scale is the root mean square: +-a entries give exactly a, a 3-4-5 vector
+    padded with zeros gives sqrt(25 / d), an all-zero token gives 1, and the result is the
+    float32 rounding of the float64 value (not a float32 running sum)."""
+    d = 128
+    signs = np.where(np.arange(d) % 3 == 0, -1.0, 1.0).astype(np.float32)
+    y = np.stack([signs * np.float32(0.375), np.zeros(d, np.float32), np.zeros(d, np.float32)])
+    y[2, 0], y[2, 1] = 3.0, 4.0
+    s = O.token_rms(y)
+    assert s[0] == np.float32(0.375)
+    assert s[1] == np.float32(1.0)
+    assert s[2] == np.float32(math.sqrt(25.0 / d))
+    rng = np.random.default_rng(11)
+    z = (rng.standard_normal((64, d)) * 1e3).astype(np.float32)
+    want = np.sqrt(np.sum(z.astype(np.float64) ** 2, axis=1) / d).astype(np.float32)
+    assert np.array_equal(O.token_rms(z), want)
+
+
 def pin_token_scale_fold():
     """Per-token scaling folds into scale/zero: codes equal those of the unscaled path except
     at rounding boundaries, and stored scale/zero agree to float32 accuracy."""

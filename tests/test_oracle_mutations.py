@@ -157,9 +157,22 @@ def m_gather_wrong_offset(mp):
     mp.setattr(O, "gather_sequence", bad)
 
 
+def m_rms_no_sqrt(mp):
+    real = O.token_rms
+    mp.setattr(O, "token_rms", lambda y: real(y) ** 2)             # mean square, not its root
+
+
+def m_rms_max_abs(mp):
+    def bad(y):
+        s = np.abs(np.asarray(y, dtype=np.float32)).max(axis=-1)   # a max-abs norm instead of the RMS
+        s[s == 0] = np.float32(1.0)
+        return s
+    mp.setattr(O, "token_rms", bad)
+
+
 MUTATIONS = [m_hadamard_sign, m_hadamard_row_order, m_rotation_norm, m_round_half_up, m_qmax_off_by_one,
              m_zero_is_max, m_pack_high_first, m_v_interleave_swapped, m_no_softmax_scale,
-             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset]
+             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
