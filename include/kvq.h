@@ -140,10 +140,10 @@ size_t kvq_paged_decode_workspace_size(
  *   softmax_scale    <= 0 selects 1 / sqrt(head_dim).
  *   out              float32 [batch][num_q_heads][head_dim], un-rotated (R applied once).
  *   workspace        device scratch of at least kvq_paged_decode_workspace_size(...) bytes
- *                    (may be NULL when that size is 0). It must be zero-filled before its first
- *                    use; every call leaves its split counters at zero again, so one zeroed
- *                    workspace serves any number of calls with the same sizes. Calls sharing a
- *                    workspace must not overlap (e.g. run them on one stream).
+ *                    (may be NULL when that size is 0) for the partial results of split
+ *                    sequences; its contents on entry do not matter and on return are
+ *                    unspecified. Calls sharing a workspace must not overlap (e.g. run them on
+ *                    one stream).
  *   pages_per_split  0 = library's choice; > 0 forces the split size (tuning and tests).
  *
  * batch == 0 is a no-op returning KVQ_OK.

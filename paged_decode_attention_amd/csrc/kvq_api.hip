@@ -27,20 +27,20 @@ float inv_sqrt(int32_t b) { return static_cast<float>(1.0 / std::sqrt(static_cas
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace of a split call: partial accumulators, (max, sum) pairs, then one counter per
-// (sequence, KV head) of splits finished - zero before the first call, reset by the kernel.
+// Workspace of a split call: the partial accumulators of every (split, sequence, query head),
+// then their (max, sum) pairs. Every entry a merge reads is written by the same call first, so
+// the contents on entry do not matter.
 struct WorkspaceLayout {
-  size_t acc_bytes, ml_offset, counter_offset, total;
+  size_t acc_bytes, ml_offset, total;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads) {
-  WorkspaceLayout w{0, 0, 0, 0};
+WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_q_heads) {
+  WorkspaceLayout w{0, 0, 0};
   if (num_splits <= 1) return w;
   const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
   w.acc_bytes = rows * kvq::kHeadDim * sizeof(float);
   w.ml_offset = round_up(w.acc_bytes);
-  w.counter_offset = w.ml_offset + round_up(rows * 2 * sizeof(float));
-  w.total = w.counter_offset + round_up(static_cast<size_t>(batch) * num_kv_heads * sizeof(unsigned));
+  w.total = w.ml_offset + round_up(rows * 2 * sizeof(float));
   return w;
 }
 
@@ -178,7 +178,7 @@ size_t kvq_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
       max_context_len < 0 || pages_per_split < 0)
     return 0;
   const kvq::SplitPlan p = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
-  return workspace_layout(p.num_splits, batch, num_q_heads, num_kv_heads).total;
+  return workspace_layout(p.num_splits, batch, num_q_heads).total;
 }
 
 kvq_status kvq_paged_decode_attention(
@@ -208,7 +208,7 @@ kvq_status kvq_paged_decode_attention(
     return KVQ_ERR_SHAPE;
 
   const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
-  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads, num_kv_heads);
+  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
 
   kvq::DecodeArgs a{};
@@ -244,7 +244,6 @@ kvq_status kvq_paged_decode_attention(
   a.pages_per_split = plan.pages_per_split;
   a.ws_acc = ws.total ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
-  a.counters = ws.total ? reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + ws.counter_offset) : nullptr;
   return kvq::launch_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

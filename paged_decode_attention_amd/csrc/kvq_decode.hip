@@ -68,7 +68,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
   const int len = min(max(a.context_lens[b], 0), a.max_context_len);
   const int n_pages = (len + ps - 1) / ps;
   const int p_begin = split * a.pages_per_split;
-  const int p_end = min(n_pages, p_begin + a.pages_per_split);
+  // the last split also takes the pages past num_splits * pages_per_split (see plan_splits)
+  const int p_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split);
   const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_q_heads + kvh * G) * kHeadDim;
 
   if (p_begin >= p_end) {
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
   const int b = live ? static_cast<int>(idx / a.num_q_heads) : 0;
   const int len = live ? min(max(a.context_lens[b], 0), a.max_context_len) : 0;
   const int n_pages = (len + a.page_size - 1) / a.page_size;
-  const int n_used = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  const int n_used = min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
 
   float mo = kNegInf;
   for (int s = 0; s < n_used; ++s) {
@@ -269,11 +270,16 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_l
     const int64_t items = static_cast<int64_t>(batch) * num_kv_heads;
     int64_t splits = (2048 + items - 1) / items;
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, (max_pages + 7) / 8));
-    pps = (max_pages + splits - 1) / splits;
-    // The matrix-core kernel walks two pages per step: an even split size keeps every split but
-    // the last free of a half-empty step. Rounding down leaves at most a short extra split (the
-    // page of the newest token) rather than a half step in every split.
+    // Split size rounded down to an even number of pages (the matrix-core kernel walks two pages
+    // per step, so only the last split can end in a half-empty step). The pages left over after
+    // the last full split go to that split when they are at most half a split (e.g. the page
+    // of the newest token); only a larger remainder gets a split of its own.
+    pps = std::max<int64_t>(1, max_pages / splits);
     if (splits > 1 && pps > 8) pps &= ~int64_t{1};
+    const int64_t full = max_pages / pps, rem = max_pages % pps;
+    p.pages_per_split = static_cast<int32_t>(pps);
+    p.num_splits = static_cast<int32_t>(std::max<int64_t>(1, full + (2 * rem > pps ? 1 : 0)));
+    return p;
   }
   pps = std::max<int64_t>(1, std::min<int64_t>(pps, max_pages));
   p.pages_per_split = static_cast<int32_t>(pps);

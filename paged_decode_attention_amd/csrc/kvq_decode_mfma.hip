@@ -225,7 +225,8 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + ps - 1) / ps;
   const int p_begin = split * a.pages_per_split;
-  const int p_end = min(n_pages, p_begin + a.pages_per_split);
+  // the last split also takes the pages past num_splits * pages_per_split (see plan_splits)
+  const int p_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split);
   const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g) * kHeadDim;
 
   if (p_begin >= p_end) {
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   const int b = static_cast<int>(pair / a.num_q_heads);
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + a.page_size - 1) / a.page_size;
-  const int nu = (n_pages + a.pages_per_split - 1) / a.pages_per_split;
+  const int nu = min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
   const LaneFwht lf = lane_fwht(a.rot, n);
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
   const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);

@@ -70,7 +70,6 @@ struct DecodeArgs {
   int32_t pages_per_split;
   float* ws_acc;                  // [num_splits][batch][num_q_heads][128]
   float* ws_ml;                   // [num_splits][batch][num_q_heads][2]  (max, sum) in log2 units
-  unsigned* counters;             // [batch][num_kv_heads] finished splits; zero between calls
 };
 
 struct DequantArgs {

@@ -168,8 +168,8 @@ def decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_c
 
 
 def decode_workspace(nbytes: int, device) -> torch.Tensor:
-    """A decode workspace of ``nbytes``: zero-filled, as the library requires before first use."""
-    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A decode workspace of ``nbytes`` (its contents do not matter to the library)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,

@@ -103,6 +103,29 @@ def test_workspace_size():
     assert L.kvq_paged_decode_workspace_size(0, 32, 8, 128, 8192, 16, 0) == 0
 
 
+def _splits(batch, hq, hkv, max_len, pps=0):
+    """Number of splits the library plans, read back from the workspace size (acc + (m, l) rows)."""
+    w = kvq.lib().kvq_paged_decode_workspace_size(batch, hq, hkv, 128, max_len, 16, pps)
+    per_split = batch * hq * 128 * 4
+    return round(w / (per_split + batch * hq * 8)) if w else 1
+
+
+def test_split_plan():
+    # Llama-3-8B decode, 4097 tokens (257 pages), 16 x 8 (sequence, KV head) items: 16 even splits of
+    # 16 pages, the 257th page joining the last split
+    assert _splits(16, 32, 8, 4097) == 16
+    assert _splits(16, 32, 8, 4096) == 16
+    # a remainder of more than half a split gets its own split: 16 * 16 + 9 pages
+    assert _splits(16, 32, 8, (16 * 16 + 9) * 16) == 17
+    # Llama-2-70B, 32769 tokens (2049 pages), 4 x 8 items: 64 splits of 32 pages
+    assert _splits(4, 64, 8, 32769) == 64
+    # enough (sequence, KV head) items to fill the GPU: no split
+    assert _splits(256, 32, 8, 8193) == 1
+    # a forced split size is taken literally
+    assert _splits(1, 32, 8, 4097, pps=16) == 17
+    assert _splits(1, 32, 8, 4097, pps=1) == 257
+
+
 def test_dequant_validation():
     L = kvq.lib()
     f = lambda **kw: L.kvq_dequant_page(NULL, NULL, kw.get("t", 0), kw.get("page", 0), kw.get("pages", 4), 8, 16, 128,

@@ -37,10 +37,14 @@ def _oracle_cache(shape, lens, plan=None, layer=0, fast=False):
 
 
 def _gpu_decode(shape, plan, dev_cache, q_bits, lens, pps=0, softmax_scale=0.0, q_prerotated=0):
+    max_len = int(max(lens)) if len(lens) else 0
+    # the workspace's contents on entry must not matter: poison it with NaN bytes
+    nbytes = kvq.decode_workspace_size(len(lens), shape.num_q_heads, shape.num_kv_heads, max_len, shape.page_size, pps)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
     out = kvq.paged_decode_attention(
         H.to_dev_bf16(q_bits), dev_cache, H.to_dev(plan.block_table), H.to_dev(np.asarray(lens, dtype=np.int32)),
-        int(max(lens)) if len(lens) else 0, shape.hadamard_block, softmax_scale=softmax_scale,
-        q_prerotated=q_prerotated, pages_per_split=pps)
+        max_len, shape.hadamard_block, softmax_scale=softmax_scale, q_prerotated=q_prerotated, workspace=ws,
+        pages_per_split=pps)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
