@@ -38,9 +38,15 @@ CFLAGS = [
 ]
 
 
+# Per-source extras. The write path never sees a NaN it must order (its min / max run on finite
+# rotated values), so NaN-honouring min / max lowering - a canonicalising move that keeps the DPP
+# row reductions from fusing into single instructions - is switched off there.
+EXTRA_CFLAGS = {"kvq_append.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_CFLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

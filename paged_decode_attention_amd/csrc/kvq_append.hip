@@ -3,151 +3,374 @@
 // rotation-quantization kernel writing straight into a paged cache; OScaR summary, zhichai.net,
 // "The OScaR Framework": Quant(S (R V)) with a per-token scale S).
 //
-// Mapping: a 16-lane row group owns one (token, head) and does both its K and its V vector;
-// lane i holds channels 8i..8i+7 (one 16-byte bf16 load per tensor). A wave covers four
-// consecutive tokens of one KV head and a 256-thread workgroup sixteen, so a page-aligned run of
-// sixteen tokens - one page-head tile of the cache - is written by one workgroup, i.e. through
-// one XCD's L2, which merges the V tile's byte-interleaved stores into whole lines before they
-// reach HBM.
+// One wave rotates and quantizes 16 consecutive tokens of one KV head, K and V. The rotation
+// y = R x is a dense contraction over the 128 channels, done on the matrix cores
+// (v_mfma_f32_16x16x32_bf16): the bf16 inputs and the +-1 (or 0) entries of R are exact bf16
+// operands, and the products accumulate in float32.
+//
+// Channel bookkeeping. Input channel m = s + 4 e + 8 G + 32 q (s: MFMA k-step 0..3, e: 0..1,
+// G: lane row 0..3, q: 16-byte load 0..3) and output channel o = n + 8 c (n: MFMA 0..7, c: lane
+// column 0..15). For the Sylvester matrix, H[m][o] is a product over the seven bit positions:
+// inside a block of b = 2^LB channels each bit contributes (-1)^(m_p o_p), outside it the
+// block-diagonal structure asks m_p == o_p. Bits 0-1 pair s with n, so that factor is uniform
+// over the wave and becomes the sign (or absence) of a whole k-step; bit 2 pairs e with n >> 2
+// and bits 3-6 pair (G, q) with c, all of which is baked into two constant B operands (one per
+// n >> 2). Each lane then ends with 8 consecutive output channels (8c .. 8c + 7) of 4 tokens
+// (rows 4G .. 4G + 3 of the MFMA output), which is exactly what the packed stores need: 4 code
+// bytes of a K row per token, and - when the 4 tokens are the 4 consecutive slots that share the
+// V tile's interleaved words - one 16-byte V store per lane.
+//
+// Quantization of the 32 values a lane holds per tensor: min / max in-lane and across the 16-lane
+// row (DPP), scale and its reciprocal computed once per token (lane c & 3 does token c & 3, then
+// quad broadcasts), codes by Markstein-corrected division (bit-exact with IEEE division), round
+// half to even. Tokens whose scale is 0 or tiny take a slower path with IEEE division and the
+// clamp; it is wave-uniform and never taken for ordinary data.
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
 namespace kvq {
 namespace {
 
-// Rotate, optionally scale per token, quantize and pack the 8 channels this lane holds (output
-// block lf.pos of the rotated vector). Returns the packed codes (INT4: 32 bits, INT2: low 16
-// bits); scale/zero are the stored values, identical in all 16 lanes of the group.
-template <int BITS, bool TOKEN_SCALE>
-__device__ __forceinline__ uint32_t rotate_quantize8(float (&x)[8], const RowFwhtPlan& rot, const LaneFwht& lf,
-                                                     float& scale, float& zero) {
-  fwht_row16_planned(x, rot, lf);
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-  float s = 1.0f;
-  if constexpr (TOKEN_SCALE) {
-    // RMS in double precision, rounded once to float (so the stored scale does not depend
-    // on the summation order), 1 for an all-zero vector.
-    double ss = 0.0;
+__device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
+
+// Factor of the block-diagonal Sylvester matrix (blocks of 2^LB) for bit position p, input bit a,
+// output bit o.
+template <int LB>
+__host__ __device__ constexpr int bit_factor(int p, int a, int o) {
+  return (p < LB) ? (((a & o) != 0) ? -1 : 1) : (a == o ? 1 : 0);
+}
+
+// Sign (+1 / -1) or absence (0) of k-step s in the MFMA of output tile n: bits 0 and 1.
+template <int LB>
+__host__ __device__ constexpr int step_sign(int s, int n) {
+  return bit_factor<LB>(0, s & 1, n & 1) * bit_factor<LB>(1, (s >> 1) & 1, (n >> 1) & 1);
+}
+
+// 1/sqrt(b) splits into 2^-(LB/2), folded into the B operand exactly, times 1/sqrt(2) for odd LB.
+template <int LB>
+__device__ __forceinline__ uint16_t b_entry(int f) {
+  constexpr uint32_t exp_bits = 127u - static_cast<uint32_t>(LB / 2);  // bf16 exponent of 2^-(LB/2)
+  return f == 0 ? uint16_t{0} : static_cast<uint16_t>(((f < 0) ? 0x8000u : 0u) | (exp_bits << 7));
+}
+
+// B operand for the output tiles with n >> 2 == n2: lane (G, c) holds rows k = 8G + r, r = 2q + e.
+template <int LB>
+__device__ __forceinline__ v4u make_b(int lane, int n2) {
+  const int G = lane >> 4, c = lane & 15;
+  const int f_lane = bit_factor<LB>(3, G & 1, c & 1) * bit_factor<LB>(4, G >> 1, (c >> 1) & 1);
+  v4u b;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ss += static_cast<double>(x[k]) * static_cast<double>(x[k]);
-    ss = row16_sum_f64(ss);
-    s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
-    if (s == 0.0f) s = 1.0f;
-    const float rs = 1.0f / s;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = div_rn(x[k], s, rs);
+  for (int q = 0; q < 4; ++q) {
+    const int f_q = f_lane * bit_factor<LB>(5, q & 1, (c >> 2) & 1) * bit_factor<LB>(6, q >> 1, c >> 3);
+    const uint32_t lo = b_entry<LB>(f_q * bit_factor<LB>(2, 0, n2));
+    const uint32_t hi = b_entry<LB>(f_q * bit_factor<LB>(2, 1, n2));
+    b[q] = lo | (hi << 16);
   }
+  return b;
+}
 
-  float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
-  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mn = row16_min(mn);
-  mx = row16_max(mx);
+// A operand of k-step s from the four 16-byte loads of one token (load q holds input channels
+// 32q + 8G + 0..7): register q = {channel s, channel s + 4} of load q.
+__device__ __forceinline__ v4u make_a(const uint4 (&x)[4], int s) {
+  const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
+  v4u a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t d[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+    a[q] = __builtin_amdgcn_perm(d[(s >> 1) + 2], d[s >> 1], sel);
+  }
+  return a;
+}
+
+// y[n][i] = (R x)[token 4G + i][channel 8c + n] for the wave's 16 tokens (before 1/sqrt(2)).
+template <int LB>
+__device__ __forceinline__ void rotate_tile(const uint4 (&x)[4], const v4u (&bop)[2], v4f (&y)[8]) {
+  v4u a[4], na[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    a[s] = make_a(x, s);
+    na[s] = a[s] ^ v4u{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    y[n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int sg = step_sign<LB>(s, n);
+      if (sg > 0) y[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a[s]), as_bf(bop[n >> 2]), y[n], 0, 0, 0);
+      if (sg < 0) y[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(na[s]), as_bf(bop[n >> 2]), y[n], 0, 0, 0);
+    }
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Value of quad lane I (every quad holds the same per-token values in its lane I).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), I * 0x55, 0xF, 0xF, true));
+}
+
+template <typename T>
+__device__ __forceinline__ T pick4(int i, T v0, T v1, T v2, T v3) {
+  return i == 0 ? v0 : i == 1 ? v1 : i == 2 ? v2 : v3;
+}
+
+constexpr float kFastMinScale = 0x1p-100f;  // below this (or 0) a token takes the guarded path
+
+// Quantize and pack the 32 values y[n][i] (token i, channel 8c + n) of one tensor. Returns the
+// packed codes of each token (INT4: 4 bytes, INT2: 2 bytes) and its stored scale and zero.
+template <int BITS, bool TOKEN_SCALE, bool ODD_LB>
+__device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&packed)[4], float (&scale)[4],
+                                              float (&zero)[4]) {
   constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
-  const float delta = (mx - mn) / kQmax;  // IEEE division (the build uses correctly rounded f32 divide)
+  if constexpr (ODD_LB) {
+    constexpr float kInvSqrt2 = 0.70710678118654752440f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[n][i] *= kInvSqrt2;
+  }
+  float s[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (TOKEN_SCALE) {
+    // RMS in double precision across the 128 channels (16 lanes x 8), rounded once to float.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double ss = 0.0;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) ss += static_cast<double>(y[n][i]) * static_cast<double>(y[n][i]);
+      ss = row16_sum_f64(ss);
+      float si = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
+      if (si == 0.0f) si = 1.0f;
+      s[i] = si;
+      const float rs = 1.0f / si;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], si, rs);
+    }
+  }
+  float mn[4], mx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float a = fminf(fminf(fminf(y[0][i], y[1][i]), fminf(y[2][i], y[3][i])),
+                    fminf(fminf(y[4][i], y[5][i]), fminf(y[6][i], y[7][i])));
+    float b = fmaxf(fmaxf(fmaxf(y[0][i], y[1][i]), fmaxf(y[2][i], y[3][i])),
+                    fmaxf(fmaxf(y[4][i], y[5][i]), fmaxf(y[6][i], y[7][i])));
+    a = fminf(a, dpp_row<kDppQuadXor1>(a));
+    b = fmaxf(b, dpp_row<kDppQuadXor1>(b));
+    a = fminf(a, dpp_row<kDppQuadXor2>(a));
+    b = fmaxf(b, dpp_row<kDppQuadXor2>(b));
+    a = fminf(a, dpp_row<kDppHalfMirror>(a));
+    b = fmaxf(b, dpp_row<kDppHalfMirror>(b));
+    a = fminf(a, dpp_row<kDppRowRor8>(a));
+    b = fmaxf(b, dpp_row<kDppRowRor8>(b));
+    mn[i] = a;
+    mx[i] = b;
+  }
+  // Scale (IEEE division) and its reciprocal: lane c computes token c & 3, quads broadcast.
+  const int own = c & 3;
+  const float d_own = pick4(own, mx[0] - mn[0], mx[1] - mn[1], mx[2] - mn[2], mx[3] - mn[3]);
+  const float delta_own = d_own / kQmax;
+  const float r_own = 1.0f / delta_own;
+  float delta[4], r[4];
+  delta[0] = quad_bcast<0>(delta_own); r[0] = quad_bcast<0>(r_own);
+  delta[1] = quad_bcast<1>(delta_own); r[1] = quad_bcast<1>(r_own);
+  delta[2] = quad_bcast<2>(delta_own); r[2] = quad_bcast<2>(r_own);
+  delta[3] = quad_bcast<3>(delta_own); r[3] = quad_bcast<3>(r_own);
 
-  uint32_t packed = 0;
-  if (delta != 0.0f) {
-    const float r = 1.0f / delta;
-    float c[8];
+  const bool fast_lane = delta[0] >= kFastMinScale && delta[1] >= kFastMinScale && delta[2] >= kFastMinScale &&
+                         delta[3] >= kFastMinScale;
+  if (__builtin_expect(__all(fast_lane), 1)) {
+    // q = RN((y - mn) / delta) exactly; q <= qmax (1 + 2^-23) and q >= 0, so rint needs no clamp.
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(rintf(div_rn(x[k] - mn, delta, r)), 0.0f), kQmax);
-    if constexpr (BITS == 4) {
+    for (int i = 0; i < 4; ++i) {
+      float cd[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        packed = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * m + 1], 16.0f, c[2 * m]), m, packed);
-    } else {
+      for (int n = 0; n < 8; ++n) cd[n] = rintf(div_rn(y[n][i] - mn[i], delta[i], r[i]));
+      uint32_t p = 0;
+      if constexpr (BITS == 4) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float b = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[4 * m + 3], 4.0f, c[4 * m + 2]), 4.0f,
-                                                      c[4 * m + 1]), 4.0f, c[4 * m]);
-        packed = __builtin_amdgcn_cvt_pk_u8_f32(b, m, packed);
+        for (int m = 0; m < 4; ++m) p = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(cd[2 * m + 1], 16.0f, cd[2 * m]), m, p);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(cd[4 * m + 3], 4.0f, cd[4 * m + 2]), 4.0f,
+                                                         cd[4 * m + 1]), 4.0f, cd[4 * m]);
+          p = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, p);
+        }
       }
+      packed[i] = p;
     }
-  }
-  scale = delta * s;
-  zero = mn * s;
-  return packed;
-}
-
-template <int BITS>
-__device__ __forceinline__ void store_k(uint8_t* tile_row, int li, uint32_t packed) {
-  if constexpr (BITS == 4) {
-    *reinterpret_cast<uint32_t*>(tile_row + li * 4) = packed;
   } else {
-    *reinterpret_cast<uint16_t*>(tile_row + li * 2) = static_cast<uint16_t>(packed);
-  }
-}
-
-// V tile: byte j of token t at ((t / 4) * row + j) * 4 + t % 4.
-template <int BITS>
-__device__ __forceinline__ void store_v(uint8_t* tile, int off, int li, uint32_t packed) {
-  constexpr int kRow = kHeadDim * BITS / 8;
-  constexpr int kBytesPerLane = 8 * BITS / 8;
-  uint8_t* base = tile + ((off >> 2) * kRow) * 4 + (off & 3);
+    // Guarded path: IEEE division, the clamp, and all-zero codes for a zero scale.
 #pragma unroll
-  for (int m = 0; m < kBytesPerLane; ++m) {
-    const int j = li * kBytesPerLane + m;
-    base[j * 4] = static_cast<uint8_t>(packed >> (8 * m));
-  }
-}
-
-template <int BITS, bool TOKEN_SCALE>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
-  constexpr int kRow = kHeadDim * BITS / 8;
-  const int lane = threadIdx.x & 63;
-  const int grp = lane >> 4;
-  const int li = lane & 15;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 6) * 4 + grp;
-  const int h = blockIdx.y;
-
-  int64_t slot = -1;
-  if (t < a.num_tokens) slot = a.slots[t];
-  const bool live = slot >= 0 && slot < a.num_slots;
-
-  uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-  if (live) {
-    kw = *reinterpret_cast<const uint4*>(a.k + t * a.k_stride + h * kHeadDim + li * 8);
-    vw = *reinterpret_cast<const uint4*>(a.v + t * a.v_stride + h * kHeadDim + li * 8);
-  }
-  float kx[8], vx[8];
-  bf16x8_to_f32(kw, kx);
-  bf16x8_to_f32(vw, vx);
-
-  // Every lane runs the transform (the DPP exchanges need all 64 lanes); dead rows store nothing.
-  const LaneFwht lf = lane_fwht(a.rot, li);
-  float ks, kz, vs, vz;
-  const uint32_t kp = rotate_quantize8<BITS, TOKEN_SCALE>(kx, a.rot, lf, ks, kz);
-  const uint32_t vp = rotate_quantize8<BITS, TOKEN_SCALE>(vx, a.rot, lf, vs, vz);
-
-  if (live) {
-    const int64_t page = slot / a.page_size;
-    const int off = static_cast<int>(slot - page * a.page_size);
-    const int64_t tile_index = page * a.num_kv_heads + h;     // (page, head) tile
-    const int64_t row_index = tile_index * a.page_size + off;  // (page, head, offset) row
-    store_k<BITS>(a.k_codes + row_index * kRow, lf.pos, kp);
-    store_v<BITS>(a.v_codes + tile_index * a.page_size * kRow, off, lf.pos, vp);
-    if (li == 0) {
-      reinterpret_cast<float2*>(a.k_sz)[row_index] = make_float2(ks, kz);
-      reinterpret_cast<float2*>(a.v_sz)[row_index] = make_float2(vs, vz);
+    for (int i = 0; i < 4; ++i) {
+      float cd[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        cd[n] = (delta[i] != 0.0f) ? fminf(fmaxf(rintf((y[n][i] - mn[i]) / delta[i]), 0.0f), kQmax) : 0.0f;
+      uint32_t p = 0;
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) p = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(cd[2 * m + 1], 16.0f, cd[2 * m]), m, p);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(cd[4 * m + 3], 4.0f, cd[4 * m + 2]), 4.0f,
+                                                         cd[4 * m + 1]), 4.0f, cd[4 * m]);
+          p = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, p);
+        }
+      }
+      packed[i] = p;
     }
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    scale[i] = delta[i] * s[i];
+    zero[i] = mn[i] * s[i];
+  }
+}
+
+// V words of four consecutive tokens: word jj = byte jj of tokens 0, 1, 2, 3 (a 4x4 byte transpose).
+__device__ __forceinline__ uint4 interleave4(const uint32_t (&p)[4]) {
+  const uint32_t x01_lo = __builtin_amdgcn_perm(p[1], p[0], 0x05010400u);
+  const uint32_t x01_hi = __builtin_amdgcn_perm(p[1], p[0], 0x07030602u);
+  const uint32_t x23_lo = __builtin_amdgcn_perm(p[3], p[2], 0x05010400u);
+  const uint32_t x23_hi = __builtin_amdgcn_perm(p[3], p[2], 0x07030602u);
+  return make_uint4(__builtin_amdgcn_perm(x23_lo, x01_lo, 0x05040100u), __builtin_amdgcn_perm(x23_lo, x01_lo, 0x07060302u),
+                    __builtin_amdgcn_perm(x23_hi, x01_hi, 0x05040100u), __builtin_amdgcn_perm(x23_hi, x01_hi, 0x07060302u));
+}
+
+template <int BITS, bool TOKEN_SCALE, int LB>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  constexpr int kRow = kHeadDim * BITS / 8;   // code bytes per token row
+  constexpr int kLaneBytes = 8 * BITS / 8;    // code bytes per lane per token (8 channels)
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+  const int64_t tile0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 16;
+  const int h = blockIdx.y;
+  if (tile0 >= a.num_tokens) return;  // whole wave past the end (uniform)
+
+  // ---- loads: lane (G, t) takes bytes 64q + 16G .. + 15 of token t's K and V head vectors
+  const int64_t tok_in = tile0 + c;
+  uint4 kx[4], vx[4];
+  if (tok_in < a.num_tokens) {
+    const uint16_t* kp = a.k + tok_in * a.k_stride + h * kHeadDim + 8 * G;
+    const uint16_t* vp = a.v + tok_in * a.v_stride + h * kHeadDim + 8 * G;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kx[q] = *reinterpret_cast<const uint4*>(kp + 32 * q);
+      vx[q] = *reinterpret_cast<const uint4*>(vp + 32 * q);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kx[q] = vx[q] = make_uint4(0, 0, 0, 0);
+  }
+  // slots of the four tokens whose outputs this lane holds
+  int64_t slot[4];
+  bool live[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = tile0 + 4 * G + i;
+    slot[i] = (t < a.num_tokens) ? a.slots[t] : -1;
+    live[i] = slot[i] >= 0 && slot[i] < a.num_slots;
+  }
+
+  const v4u bop[2] = {make_b<LB>(lane, 0), make_b<LB>(lane, 1)};
+  uint32_t kp[4], vp[4];
+  float ks[4], kz[4], vs[4], vz[4];
+  {
+    v4f y[8];
+    rotate_tile<LB>(kx, bop, y);
+    quantize_tile<BITS, TOKEN_SCALE, (LB & 1) != 0>(y, c, kp, ks, kz);
+  }
+  {
+    v4f y[8];
+    rotate_tile<LB>(vx, bop, y);
+    quantize_tile<BITS, TOKEN_SCALE, (LB & 1) != 0>(y, c, vp, vs, vz);
+  }
+
+  // ---- stores
+  const int ps = a.page_size;
+  int64_t row_index[4];  // (page, head, offset) row of each token
+  int64_t tile_index[4];
+  int off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t s = live[i] ? slot[i] : 0;
+    const int64_t page = s / ps;
+    off[i] = static_cast<int>(s - page * ps);
+    tile_index[i] = page * a.num_kv_heads + h;
+    row_index[i] = tile_index[i] * ps + off[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!live[i]) continue;
+    uint8_t* krow = a.k_codes + row_index[i] * kRow + kLaneBytes * c;
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint32_t*>(krow) = kp[i];
+    } else {
+      *reinterpret_cast<uint16_t*>(krow) = static_cast<uint16_t>(kp[i]);
+    }
+    if (c == i) reinterpret_cast<float2*>(a.k_sz)[row_index[i]] = make_float2(ks[i], kz[i]);
+    if (c == 4 + i) reinterpret_cast<float2*>(a.v_sz)[row_index[i]] = make_float2(vs[i], vz[i]);
+  }
+  // V: whole interleaved words when the four tokens fill one word group of a tile, else bytes.
+  const bool group = live[0] && live[1] && live[2] && live[3] && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
+                     slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+  if (group) {
+    uint8_t* dst = a.v_codes + tile_index[0] * ps * kRow + ((off[0] >> 2) * kRow + kLaneBytes * c) * 4;
+    const uint4 w = interleave4(vp);
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint4*>(dst) = w;
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w.x, w.y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!live[i]) continue;
+      uint8_t* base = a.v_codes + tile_index[i] * ps * kRow + ((off[i] >> 2) * kRow + kLaneBytes * c) * 4 + (off[i] & 3);
+#pragma unroll
+      for (int m = 0; m < kLaneBytes; ++m) base[4 * m] = static_cast<uint8_t>(vp[i] >> (8 * m));
+    }
+  }
+}
+
+template <int BITS, bool TS>
+hipError_t launch_lb(const AppendArgs& a, int lb, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  switch (lb) {
+    case 0: hipLaunchKernelGGL((append_kernel<BITS, TS, 0>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((append_kernel<BITS, TS, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((append_kernel<BITS, TS, 2>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((append_kernel<BITS, TS, 3>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((append_kernel<BITS, TS, 4>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((append_kernel<BITS, TS, 5>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((append_kernel<BITS, TS, 6>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((append_kernel<BITS, TS, 7>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((a.num_tokens + 15) / 16), static_cast<unsigned>(a.num_kv_heads));
-  const dim3 block(256);
-  if (a.bits == 4 && !a.token_scale) {
-    hipLaunchKernelGGL((append_kernel<4, false>), grid, block, 0, stream, a);
-  } else if (a.bits == 4) {
-    hipLaunchKernelGGL((append_kernel<4, true>), grid, block, 0, stream, a);
-  } else if (!a.token_scale) {
-    hipLaunchKernelGGL((append_kernel<2, false>), grid, block, 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((append_kernel<2, true>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  // four waves of 16 tokens per workgroup
+  const dim3 grid(static_cast<unsigned>((a.num_tokens + 63) / 64), static_cast<unsigned>(a.num_kv_heads));
+  int lb = 0;
+  while ((1 << lb) < a.rot.hb) ++lb;
+  if (a.bits == 4 && !a.token_scale) return launch_lb<4, false>(a, lb, grid, stream);
+  if (a.bits == 4) return launch_lb<4, true>(a, lb, grid, stream);
+  if (!a.token_scale) return launch_lb<2, false>(a, lb, grid, stream);
+  return launch_lb<2, true>(a, lb, grid, stream);
 }
 
 }  // namespace kvq
