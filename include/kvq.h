@@ -38,6 +38,9 @@
  *   - Return value: KVQ_OK, or the first failed check (nothing is launched then), or
  *     KVQ_ERR_HIP if the launch itself failed. No C++ exception crosses the ABI.
  *   - head_dim must be 128 and page_size a multiple of 16 (KVQ_ERR_UNSUPPORTED otherwise).
+ *   - Alignment (KVQ_ERR_SHAPE otherwise): k, v, q, out, k_codes and v_codes 16 bytes (the
+ *     codes argument of kvq_dequant_page 4); slot_mapping, k_sz, v_sz 8; block_table and
+ *     context_lens 4; token strides a multiple of 8 elements.
  *
  * Rotation R (block size b, a power of two dividing head_dim; b = 1 is no rotation, i.e.
  * plain INT4): R = blockdiag(H_b, ..., H_b) / sqrt(b), H_b the Sylvester Hadamard matrix
@@ -98,6 +101,7 @@ const char* kvq_status_string(int32_t status);
  *   slot_mapping     int64 [num_tokens]: destination slot of token i; a negative slot skips
  *                    the token; slots >= num_pages * page_size are ignored as well. Two
  *                    tokens with the same slot in one call race (undefined result).
+ *                    num_pages * page_size must stay below 2^32 (KVQ_ERR_UNSUPPORTED).
  *   k_codes, v_codes, k_sz, v_sz   the cache, layout above; only the addressed rows change.
  *   hadamard_block   b: power of two dividing head_dim (1 = no rotation).
  *   bits             4 (INT4) or 2 (INT2).

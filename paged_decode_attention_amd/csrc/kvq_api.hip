@@ -145,11 +145,17 @@ kvq_status kvq_rotate_quantize_append(
   const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (k_token_stride < row_elems || v_token_stride < row_elems) return KVQ_ERR_SHAPE;
   if (k_token_stride % 8 || v_token_stride % 8) return KVQ_ERR_SHAPE;
-  if (num_kv_heads > 65535 || (num_tokens + 15) / 16 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || num_tokens > (int64_t{1} << 36) ||
+      ((num_tokens + 15) / 16) * num_kv_heads > 0x7FFFFFFF)
+    return KVQ_ERR_UNSUPPORTED;
+  // 32-bit slots and rows per page
+  if (static_cast<int64_t>(num_pages) * page_size > 0xFFFFFFFFll ||
+      static_cast<int64_t>(num_kv_heads) * page_size > 0xFFFFFFFFll)
+    return KVQ_ERR_UNSUPPORTED;
   if (num_tokens == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping || !k_codes || !v_codes || !k_sz || !v_sz) return KVQ_ERR_NULL;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(k_codes, 4) ||
-      !aligned(v_codes, 4) || !aligned(k_sz, 8) || !aligned(v_sz, 8))
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(k_codes, 16) ||
+      !aligned(v_codes, 16) || !aligned(k_sz, 8) || !aligned(v_sz, 8))
     return KVQ_ERR_SHAPE;
 
   kvq::AppendArgs a{};
@@ -166,6 +172,16 @@ kvq_status kvq_rotate_quantize_append(
   a.v_sz = v_sz;
   a.num_slots = static_cast<int64_t>(num_pages) * page_size;
   a.page_size = page_size;
+  // Division by the invariant page size for 32-bit slots (Granlund-Montgomery, round-up
+  // multiplier): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, then
+  // n / d = (t + ((n - t) >> 1)) >> (l - 1) with t = umulhi(m, n), for every n < 2^32.
+  {
+    int l = 0;
+    while ((int64_t{1} << l) < page_size) ++l;
+    const uint64_t d = static_cast<uint64_t>(page_size);
+    a.ps_magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+    a.ps_shift = l - 1;
+  }
   a.rot = kvq::make_row_fwht_plan(hadamard_block);
   a.bits = bits;
   a.token_scale = token_scale;

@@ -25,6 +25,8 @@
 // quad broadcasts), codes by Markstein-corrected division (bit-exact with IEEE division), round
 // half to even. Tokens whose scale is 0 or tiny take a slower path with IEEE division and the
 // clamp; it is wave-uniform and never taken for ordinary data.
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
@@ -52,25 +54,37 @@ __host__ __device__ constexpr int step_sign(int s, int n) {
 
 // 1/sqrt(b) splits into 2^-(LB/2), folded into the B operand exactly, times 1/sqrt(2) for odd LB.
 template <int LB>
-__device__ __forceinline__ uint16_t b_entry(int f) {
+constexpr uint32_t b_entry(int f) {
   constexpr uint32_t exp_bits = 127u - static_cast<uint32_t>(LB / 2);  // bf16 exponent of 2^-(LB/2)
-  return f == 0 ? uint16_t{0} : static_cast<uint16_t>(((f < 0) ? 0x8000u : 0u) | (exp_bits << 7));
+  return f == 0 ? 0u : (((f < 0) ? 0x8000u : 0u) | (exp_bits << 7));
 }
 
 // B operand for the output tiles with n >> 2 == n2: lane (G, c) holds rows k = 8G + r, r = 2q + e.
 template <int LB>
-__device__ __forceinline__ v4u make_b(int lane, int n2) {
+constexpr uint32_t b_word(int lane, int n2, int q) {
   const int G = lane >> 4, c = lane & 15;
-  const int f_lane = bit_factor<LB>(3, G & 1, c & 1) * bit_factor<LB>(4, G >> 1, (c >> 1) & 1);
-  v4u b;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int f_q = f_lane * bit_factor<LB>(5, q & 1, (c >> 2) & 1) * bit_factor<LB>(6, q >> 1, c >> 3);
-    const uint32_t lo = b_entry<LB>(f_q * bit_factor<LB>(2, 0, n2));
-    const uint32_t hi = b_entry<LB>(f_q * bit_factor<LB>(2, 1, n2));
-    b[q] = lo | (hi << 16);
+  const int f = bit_factor<LB>(3, G & 1, c & 1) * bit_factor<LB>(4, G >> 1, (c >> 1) & 1) *
+                bit_factor<LB>(5, q & 1, (c >> 2) & 1) * bit_factor<LB>(6, q >> 1, c >> 3);
+  return b_entry<LB>(f * bit_factor<LB>(2, 0, n2)) | (b_entry<LB>(f * bit_factor<LB>(2, 1, n2)) << 16);
+}
+
+// All B operands, built at compile time: [n2][lane][q] for each block size.
+template <int LB>
+struct BTable {
+  uint32_t w[2][64][4];
+  constexpr BTable() : w() {
+    for (int n2 = 0; n2 < 2; ++n2)
+      for (int l = 0; l < 64; ++l)
+        for (int q = 0; q < 4; ++q) w[n2][l][q] = b_word<LB>(l, n2, q);
   }
-  return b;
+};
+template <int LB>
+__device__ constexpr BTable<LB> kBTable{};
+
+template <int LB>
+__device__ __forceinline__ v4u load_b(int lane, int n2) {
+  const uint4 x = *reinterpret_cast<const uint4*>(kBTable<LB>.w[n2][lane]);
+  return v4u{x.x, x.y, x.z, x.w};
 }
 
 // A operand of k-step s from the four 16-byte loads of one token (load q holds input channels
@@ -158,10 +172,15 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   float mn[4], mx[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float a = fminf(fminf(fminf(y[0][i], y[1][i]), fminf(y[2][i], y[3][i])),
-                    fminf(fminf(y[4][i], y[5][i]), fminf(y[6][i], y[7][i])));
-    float b = fmaxf(fmaxf(fmaxf(y[0][i], y[1][i]), fmaxf(y[2][i], y[3][i])),
-                    fmaxf(fmaxf(y[4][i], y[5][i]), fmaxf(y[6][i], y[7][i])));
+    // chains of three-input min / max: 8 values in 4 instructions each
+    float a = fminf(fminf(y[0][i], y[1][i]), y[2][i]);
+    float b = fmaxf(fmaxf(y[0][i], y[1][i]), y[2][i]);
+    a = fminf(fminf(a, y[3][i]), y[4][i]);
+    b = fmaxf(fmaxf(b, y[3][i]), y[4][i]);
+    a = fminf(fminf(a, y[5][i]), y[6][i]);
+    b = fmaxf(fmaxf(b, y[5][i]), y[6][i]);
+    a = fminf(a, y[7][i]);
+    b = fmaxf(b, y[7][i]);
     a = fminf(a, dpp_row<kDppQuadXor1>(a));
     b = fmaxf(b, dpp_row<kDppQuadXor1>(b));
     a = fminf(a, dpp_row<kDppQuadXor2>(a));
@@ -173,10 +192,14 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
     mn[i] = a;
     mx[i] = b;
   }
-  // Scale (IEEE division) and its reciprocal: lane c computes token c & 3, quads broadcast.
+  // Scale and its reciprocal: lane c computes token c & 3, then quads broadcast. The scale
+  // RN(d / qmax) comes from Markstein's correction with the constant RN(1 / qmax) - equal to IEEE
+  // division for every normal d (checked exhaustively over all significands); smaller scales take
+  // the guarded path, which divides again.
   const int own = c & 3;
   const float d_own = pick4(own, mx[0] - mn[0], mx[1] - mn[1], mx[2] - mn[2], mx[3] - mn[3]);
-  const float delta_own = d_own / kQmax;
+  constexpr float kInvQmax = 1.0f / kQmax;
+  const float delta_own = div_rn(d_own, kQmax, kInvQmax);
   const float r_own = 1.0f / delta_own;
   float delta[4], r[4];
   delta[0] = quad_bcast<0>(delta_own); r[0] = quad_bcast<0>(r_own);
@@ -184,9 +207,8 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   delta[2] = quad_bcast<2>(delta_own); r[2] = quad_bcast<2>(r_own);
   delta[3] = quad_bcast<3>(delta_own); r[3] = quad_bcast<3>(r_own);
 
-  const bool fast_lane = delta[0] >= kFastMinScale && delta[1] >= kFastMinScale && delta[2] >= kFastMinScale &&
-                         delta[3] >= kFastMinScale;
-  if (__builtin_expect(__all(fast_lane), 1)) {
+  // every token of the wave is some lane's own token
+  if (__builtin_expect(__all(delta_own >= kFastMinScale), 1)) {
     // q = RN((y - mn) / delta) exactly; q <= qmax (1 + 2^-23) and q >= 0, so rint needs no clamp.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -211,6 +233,7 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
     // Guarded path: IEEE division, the clamp, and all-zero codes for a zero scale.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      delta[i] = (mx[i] - mn[i]) / kQmax;
       float cd[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n)
@@ -247,86 +270,83 @@ __device__ __forceinline__ uint4 interleave4(const uint32_t (&p)[4]) {
                     __builtin_amdgcn_perm(x23_hi, x01_hi, 0x05040100u), __builtin_amdgcn_perm(x23_hi, x01_hi, 0x07060302u));
 }
 
+// Inputs of one work item (16 tokens of one KV head): lane (G, t) holds bytes 64q + 16G .. + 15
+// of token t's K and V head vectors, and the slots of tokens 4G .. 4G + 3.
+struct TileInputs {
+  uint4 kx[4], vx[4];
+  int64_t slot[4];
+};
+
+__device__ __forceinline__ void load_tile(const AppendArgs& a, int64_t tile0, int h, int G, int c, TileInputs& in) {
+  // Rows past the last token re-read the last one: MFMA rows are independent tokens, and those
+  // rows are never stored.
+  const int64_t last = a.num_tokens - 1;
+  const int64_t tok_in = min(tile0 + c, last);
+  const uint16_t* kp = a.k + tok_in * a.k_stride + h * kHeadDim + 8 * G;
+  const uint16_t* vp = a.v + tok_in * a.v_stride + h * kHeadDim + 8 * G;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    in.kx[q] = *reinterpret_cast<const uint4*>(kp + 32 * q);
+    in.vx[q] = *reinterpret_cast<const uint4*>(vp + 32 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) in.slot[i] = a.slots[min(tile0 + 4 * G + i, last)];
+}
+
 template <int BITS, bool TOKEN_SCALE, int LB>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+__device__ __forceinline__ void process_tile(const AppendArgs& a, int64_t tile0, int h, int c, const v4u (&bop)[2],
+                                             const TileInputs& in) {
   constexpr int kRow = kHeadDim * BITS / 8;   // code bytes per token row
   constexpr int kLaneBytes = 8 * BITS / 8;    // code bytes per lane per token (8 channels)
-  const int lane = threadIdx.x & 63;
-  const int G = lane >> 4;
-  const int c = lane & 15;
-  const int64_t tile0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 16;
-  const int h = blockIdx.y;
-  if (tile0 >= a.num_tokens) return;  // whole wave past the end (uniform)
-
-  // ---- loads: lane (G, t) takes bytes 64q + 16G .. + 15 of token t's K and V head vectors
-  const int64_t tok_in = tile0 + c;
-  uint4 kx[4], vx[4];
-  if (tok_in < a.num_tokens) {
-    const uint16_t* kp = a.k + tok_in * a.k_stride + h * kHeadDim + 8 * G;
-    const uint16_t* vp = a.v + tok_in * a.v_stride + h * kHeadDim + 8 * G;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      kx[q] = *reinterpret_cast<const uint4*>(kp + 32 * q);
-      vx[q] = *reinterpret_cast<const uint4*>(vp + 32 * q);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kx[q] = vx[q] = make_uint4(0, 0, 0, 0);
-  }
-  // slots of the four tokens whose outputs this lane holds
-  int64_t slot[4];
-  bool live[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = tile0 + 4 * G + i;
-    slot[i] = (t < a.num_tokens) ? a.slots[t] : -1;
-    live[i] = slot[i] >= 0 && slot[i] < a.num_slots;
-  }
-
-  const v4u bop[2] = {make_b<LB>(lane, 0), make_b<LB>(lane, 1)};
+  const int G = (threadIdx.x & 63) >> 4;
   uint32_t kp[4], vp[4];
   float ks[4], kz[4], vs[4], vz[4];
   {
     v4f y[8];
-    rotate_tile<LB>(kx, bop, y);
+    rotate_tile<LB>(in.kx, bop, y);
     quantize_tile<BITS, TOKEN_SCALE, (LB & 1) != 0>(y, c, kp, ks, kz);
   }
   {
     v4f y[8];
-    rotate_tile<LB>(vx, bop, y);
+    rotate_tile<LB>(in.vx, bop, y);
     quantize_tile<BITS, TOKEN_SCALE, (LB & 1) != 0>(y, c, vp, vs, vz);
   }
 
-  // ---- stores
-  const int ps = a.page_size;
-  int64_t row_index[4];  // (page, head, offset) row of each token
-  int64_t tile_index[4];
-  int off[4];
+  // ---- stores. Row r = (page * H + h) * ps + off of the cache; a K row starts at r * kRow, the
+  // V word group of offsets off & ~3 at (r - (off & 3)) * kRow, the scale/zero pair at 8 r.
+  const uint32_t ps = static_cast<uint32_t>(a.page_size);
+  const uint32_t page_rows = static_cast<uint32_t>(a.num_kv_heads) * ps;  // rows per page (< 2^32: checked)
+  const uint32_t head_row = static_cast<uint32_t>(h) * ps;
+  bool live[4];
+  uint64_t row[4];
+  uint32_t off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t s = live[i] ? slot[i] : 0;
-    const int64_t page = s / ps;
-    off[i] = static_cast<int>(s - page * ps);
-    tile_index[i] = page * a.num_kv_heads + h;
-    row_index[i] = tile_index[i] * ps + off[i];
+    live[i] = tile0 + 4 * G + i < a.num_tokens && in.slot[i] >= 0 && in.slot[i] < a.num_slots;
+    const uint32_t s = live[i] ? static_cast<uint32_t>(in.slot[i]) : 0u;  // live slots are < 2^32
+    const uint32_t t = __umulhi(s, a.ps_magic);
+    const uint32_t page = (t + ((s - t) >> 1)) >> a.ps_shift;
+    off[i] = s - page * ps;
+    row[i] = static_cast<uint64_t>(page) * page_rows + (head_row + off[i]);
   }
+  uint8_t* const k_lane = a.k_codes + kLaneBytes * c;
+  uint8_t* const v_lane = a.v_codes + 4 * kLaneBytes * c;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!live[i]) continue;
-    uint8_t* krow = a.k_codes + row_index[i] * kRow + kLaneBytes * c;
     if constexpr (BITS == 4) {
-      *reinterpret_cast<uint32_t*>(krow) = kp[i];
+      *reinterpret_cast<uint32_t*>(k_lane + row[i] * kRow) = kp[i];
     } else {
-      *reinterpret_cast<uint16_t*>(krow) = static_cast<uint16_t>(kp[i]);
+      *reinterpret_cast<uint16_t*>(k_lane + row[i] * kRow) = static_cast<uint16_t>(kp[i]);
     }
-    if (c == i) reinterpret_cast<float2*>(a.k_sz)[row_index[i]] = make_float2(ks[i], kz[i]);
-    if (c == 4 + i) reinterpret_cast<float2*>(a.v_sz)[row_index[i]] = make_float2(vs[i], vz[i]);
+    if (c == i) reinterpret_cast<float2*>(a.k_sz)[row[i]] = make_float2(ks[i], kz[i]);
+    if (c == 4 + i) reinterpret_cast<float2*>(a.v_sz)[row[i]] = make_float2(vs[i], vz[i]);
   }
   // V: whole interleaved words when the four tokens fill one word group of a tile, else bytes.
-  const bool group = live[0] && live[1] && live[2] && live[3] && (slot[0] & 3) == 0 && slot[1] == slot[0] + 1 &&
-                     slot[2] == slot[0] + 2 && slot[3] == slot[0] + 3;
+  const bool group = live[0] && live[1] && live[2] && live[3] && (in.slot[0] & 3) == 0 &&
+                     in.slot[1] == in.slot[0] + 1 && in.slot[2] == in.slot[0] + 2 && in.slot[3] == in.slot[0] + 3;
   if (group) {
-    uint8_t* dst = a.v_codes + tile_index[0] * ps * kRow + ((off[0] >> 2) * kRow + kLaneBytes * c) * 4;
+    uint8_t* dst = v_lane + row[0] * kRow;
     const uint4 w = interleave4(vp);
     if constexpr (BITS == 4) {
       *reinterpret_cast<uint4*>(dst) = w;
@@ -337,40 +357,77 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (!live[i]) continue;
-      uint8_t* base = a.v_codes + tile_index[i] * ps * kRow + ((off[i] >> 2) * kRow + kLaneBytes * c) * 4 + (off[i] & 3);
+      const uint32_t sub = off[i] & 3;
+      uint8_t* base = v_lane + (row[i] - sub) * kRow + sub;
 #pragma unroll
       for (int m = 0; m < kLaneBytes; ++m) base[4 * m] = static_cast<uint8_t>(vp[i] >> (8 * m));
     }
   }
 }
 
-template <int BITS, bool TS>
-hipError_t launch_lb(const AppendArgs& a, int lb, dim3 grid, hipStream_t stream) {
-  const dim3 block(256);
-  switch (lb) {
-    case 0: hipLaunchKernelGGL((append_kernel<BITS, TS, 0>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((append_kernel<BITS, TS, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((append_kernel<BITS, TS, 2>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((append_kernel<BITS, TS, 3>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((append_kernel<BITS, TS, 4>), grid, block, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((append_kernel<BITS, TS, 5>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((append_kernel<BITS, TS, 6>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((append_kernel<BITS, TS, 7>), grid, block, 0, stream, a); break;
-  }
+#ifndef KVQ_APPEND_HEAD_FASTEST
+#define KVQ_APPEND_HEAD_FASTEST 1
+#endif
+
+// One wave per work item of 16 tokens x one KV head, all loads issued before any arithmetic.
+// Items are numbered head-fastest (w = tile * H + h), so the waves that run together read the
+// same tokens' rows of all heads (one contiguous stretch of the K/V inputs) and write the
+// neighbouring page-head tiles of the cache.
+template <int BITS, bool TOKEN_SCALE, int LB>
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int64_t num_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4;
+  const int c = lane & 15;
+  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t H = static_cast<uint32_t>(a.num_kv_heads);
+#if KVQ_APPEND_HEAD_FASTEST
+  const int64_t tile = w / H;
+  const int h = static_cast<int>(w % H);
+#else
+  const uint32_t tiles32 = static_cast<uint32_t>(num_tiles);
+  const int64_t tile = w % tiles32;
+  const int h = static_cast<int>(w / tiles32);
+#endif
+  if (tile >= num_tiles || h >= a.num_kv_heads) return;  // uniform per wave
+  const v4u bop[2] = {load_b<LB>(lane, 0), load_b<LB>(lane, 1)};
+  TileInputs in;
+  load_tile(a, tile * 16, h, G, c, in);
+  __builtin_amdgcn_sched_barrier(0);  // issue every load (K, V, slots) before any arithmetic
+  process_tile<BITS, TOKEN_SCALE, LB>(a, tile * 16, h, c, bop, in);
+}
+
+template <int BITS, bool TS, int LB>
+hipError_t launch_one(const AppendArgs& a, hipStream_t stream) {
+  const int64_t tiles = (a.num_tokens + 15) / 16;
+  const int64_t items = tiles * a.num_kv_heads;  // < 2^31 (checked by the caller)
+  hipLaunchKernelGGL((append_kernel<BITS, TS, LB>), dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, stream,
+                     a, tiles);
   return hipGetLastError();
+}
+
+template <int BITS, bool TS>
+hipError_t launch_lb(const AppendArgs& a, int lb, hipStream_t stream) {
+  switch (lb) {
+    case 0: return launch_one<BITS, TS, 0>(a, stream);
+    case 1: return launch_one<BITS, TS, 1>(a, stream);
+    case 2: return launch_one<BITS, TS, 2>(a, stream);
+    case 3: return launch_one<BITS, TS, 3>(a, stream);
+    case 4: return launch_one<BITS, TS, 4>(a, stream);
+    case 5: return launch_one<BITS, TS, 5>(a, stream);
+    case 6: return launch_one<BITS, TS, 6>(a, stream);
+    default: return launch_one<BITS, TS, 7>(a, stream);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
-  // four waves of 16 tokens per workgroup
-  const dim3 grid(static_cast<unsigned>((a.num_tokens + 63) / 64), static_cast<unsigned>(a.num_kv_heads));
   int lb = 0;
   while ((1 << lb) < a.rot.hb) ++lb;
-  if (a.bits == 4 && !a.token_scale) return launch_lb<4, false>(a, lb, grid, stream);
-  if (a.bits == 4) return launch_lb<4, true>(a, lb, grid, stream);
-  if (!a.token_scale) return launch_lb<2, false>(a, lb, grid, stream);
-  return launch_lb<2, true>(a, lb, grid, stream);
+  if (a.bits == 4 && !a.token_scale) return launch_lb<4, false>(a, lb, stream);
+  if (a.bits == 4) return launch_lb<4, true>(a, lb, stream);
+  if (!a.token_scale) return launch_lb<2, false>(a, lb, stream);
+  return launch_lb<2, true>(a, lb, stream);
 }
 
 }  // namespace kvq

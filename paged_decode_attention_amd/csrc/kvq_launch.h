@@ -38,8 +38,10 @@ struct AppendArgs {
   uint8_t* v_codes;
   float* k_sz;
   float* v_sz;
-  int64_t num_slots;              // num_pages * page_size
+  int64_t num_slots;              // num_pages * page_size (< 2^32)
   int32_t page_size;
+  uint32_t ps_magic;              // slot / page_size = (hi + ((slot - hi) >> 1)) >> ps_shift,
+  int32_t ps_shift;               //   hi = umulhi(slot, ps_magic)  (32-bit slots)
   RowFwhtPlan rot;                // the rotation (Hadamard block size and lane plan)
   int32_t bits;
   int32_t token_scale;
