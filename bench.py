@@ -47,6 +47,10 @@ def parse_args():
                    help="short program for rocprofv3 --pmc passes: a 256 MiB calibration copy, then --steps steps")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="print the HBM traffic summary of two rocprofv3 --pmc runs of --counters")
+    p.add_argument("--suite", action="store_true",
+                   help="time every workload shape (tiny, batch sweep with and without rotation, the 80-layer "
+                        "Llama-2-70B step, the chunked OScaR INT2 prefill) and print one JSON line each")
+    p.add_argument("--suite-cpu", action="store_true", help="with --suite: also time the CPU oracle on small samples")
     p.add_argument("--summarize-kernel-stats", metavar="RUN_DIR",
                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run as markdown")
     return p.parse_args()
@@ -223,6 +227,243 @@ def cpu_baseline(shape, k, v, slots, plan, q) -> dict:
     }
 
 
+# ----------------------------------------------------------------------------- workload suite
+
+def _cache_bytes(shape, num_pages) -> int:
+    return num_pages * shape.num_kv_heads * shape.page_size * (2 * 128 * shape.bits // 8 + 16)
+
+
+def _timed(fn, n, stream):
+    """Average ms of fn(i) over n back-to-back calls (events on the launch stream)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def _filled_caches(shape, plan, n_copies, dev, stream, layer=0):
+    """n_copies caches holding the whole prefill of ``shape`` (device-drawn inputs)."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    seq, pos = W.prefill_order(shape)
+    slots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, seq, pos)).to(dev)
+    k, v = W.draw_kv_device(shape, len(seq), dev, layer=layer)
+    caches = []
+    for _ in range(n_copies):
+        c = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+        kvq.rotate_quantize_append(k, v, slots, c, shape.hadamard_block, shape.token_scale, stream=stream)
+        caches.append(c)
+    del k, v
+    torch.cuda.synchronize()
+    return caches
+
+
+def _decode_step_fns(shape, plan, caches, dev, stream, layer=0):
+    """(append, attend) closures for one decode step of ``shape`` on cache copy i."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    dseq, dpos = W.decode_positions(shape)
+    dslots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, dseq, dpos)).to(dev)
+    kn, vn = W.draw_kv_device(shape, shape.batch, dev, layer=layer, stream="decode")
+    q = W.draw_q_device(shape, dev, layer=layer)
+    lens = np.asarray(shape.context_lens, dtype=np.int32) + 1
+    lens_d = torch.from_numpy(lens).to(dev)
+    bt = torch.from_numpy(plan.block_table).to(dev)
+    max_len = int(lens.max())
+    ws = kvq.decode_workspace(kvq.decode_workspace_size(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
+                                                        shape.page_size), dev)
+    out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def append(i):
+        kvq.rotate_quantize_append(kn, vn, dslots, caches[i % len(caches)], shape.hadamard_block, shape.token_scale,
+                                   stream=stream)
+
+    def attend(i):
+        kvq.paged_decode_attention(q, caches[i % len(caches)], bt, lens_d, max_len, shape.hadamard_block, out=out,
+                                   workspace=ws, stream=stream)
+    return append, attend, lens
+
+
+def _line(**kw):
+    return kw
+
+
+def suite_sweep(dev, stream, cpu):
+    from paged_decode_attention_amd import workloads as W
+    rows = []
+    for b in (1, 8, 32, 128, 256):
+        for hb in (64, 1):
+            shape = W.config(f"sweep_b{b}", hadamard_block=hb)
+            plan = W.plan_pages(shape, extra_tokens=1)
+            n_copies = int(min(32, max(1, math.ceil(1.1e9 / _cache_bytes(shape, plan.num_pages)))))
+            caches = _filled_caches(shape, plan, n_copies, dev, stream)
+            append, attend, lens = _decode_step_fns(shape, plan, caches, dev, stream)
+            for i in range(5):
+                append(i), attend(i)
+            n = 60
+            t_app = _timed(append, n, stream)
+            t_att = _timed(attend, n, stream)
+            t_step = _timed(lambda i: (append(i), attend(i)), n, stream)
+            b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+            b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits)
+            rows.append(_line(workload=f"sweep batch {b}, Hadamard block {hb}" + (" (plain INT4)" if hb == 1 else ""),
+                              batch=b, hadamard_block=hb, cache_copies=n_copies, step_ms=round(t_step, 5),
+                              append_ms=round(t_app, 5), attention_ms=round(t_att, 5),
+                              attention_GBps=round(b_att / t_att / 1e6, 1),
+                              step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
+                              tokens_per_s=round(b / (t_step * 1e-3), 1)))
+            del caches
+            if cpu and hb == 64 and b <= 8:
+                rows[-1]["cpu_oracle"] = _cpu_decode_sample(shape, n_seq=min(b, 2))
+    return rows
+
+
+def suite_llama2_70b(dev, stream, cpu):
+    """80 independent per-layer caches; one step = per layer, append one token per sequence and
+    attend (a new query per layer)."""
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("llama2_70b")
+    layers = []
+    for l in range(shape.layers):
+        plan = W.plan_pages(shape, extra_tokens=1, layer=l)
+        caches = _filled_caches(shape, plan, 1, dev, stream, layer=l)
+        layers.append(_decode_step_fns(shape, plan, caches, dev, stream, layer=l))
+        if l % 20 == 19:
+            print(f"llama2_70b: {l + 1} layer caches filled", file=sys.stderr, flush=True)
+
+    def step(i):
+        for append, attend, _ in layers:
+            append(0)
+            attend(0)
+
+    def attention_only(i):
+        for _, attend, _ in layers:
+            attend(0)
+    for i in range(2):
+        step(i)
+    t_step = _timed(step, 10, stream)
+    t_att = _timed(attention_only, 10, stream)
+    lens = layers[0][2]
+    b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size) * shape.layers
+    b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits) * shape.layers
+    row = _line(workload="Llama-2-70B shape, 4 x 32768 tokens, 64/8 heads, 80 layers (one step)", batch=shape.batch,
+                layers=shape.layers, step_ms=round(t_step, 4), attention_ms_80_layers=round(t_att, 4),
+                attention_ms_per_layer=round(t_att / shape.layers, 5), attention_GBps=round(b_att / t_att / 1e6, 1),
+                step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
+                tokens_per_s=round(shape.batch / (t_step * 1e-3), 1))
+    if cpu:
+        c = _cpu_decode_sample(shape, n_seq=1)
+        c["extrapolated_step_s"] = round(c["seconds_per_seq"] * shape.batch * shape.layers, 1)
+        row["cpu_oracle"] = c
+    return [row]
+
+
+def suite_oscar(dev, stream, cpu):
+    """Chunked prefill (first 1..15 tokens, then 512-token chunks that start mid-page), then a decode step."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("oscar_int2")
+    plan = W.plan_pages(shape, extra_tokens=1)
+    calls = W.chunk_schedule(shape)
+    n_tok = sum(len(s) for s, _ in calls)
+    k, v = W.draw_kv_device(shape, n_tok, dev)
+    cache = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+    slot_list, offs, o = [], [], 0
+    for sq, ps in calls:
+        slot_list.append(torch.from_numpy(W.slots_for_positions(plan, shape.page_size, sq, ps)).to(dev))
+        offs.append((o, o + len(sq)))
+        o += len(sq)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    chunk_ms = []
+    for (a, b), sl in zip(offs, slot_list):
+        e0.record(stream)
+        kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        chunk_ms.append(e0.elapsed_time(e1))
+    del k, v
+    full = [t for (a, b), t in zip(offs, chunk_ms) if b - a == shape.batch * shape.chunk]
+    # attention cycles over 8 copies (1.3 GB) so that the 256 MB last-level cache cannot serve it
+    copies = [cache] + [kvq.PagedKVCache(cache.k_codes.clone(), cache.v_codes.clone(), cache.k_sz.clone(),
+                                         cache.v_sz.clone(), cache.bits) for _ in range(7)]
+    append, attend, lens = _decode_step_fns(shape, plan, copies, dev, stream)
+    for i in range(5):
+        attend(i)
+    t_att = _timed(attend, 50, stream)
+    t_app = _timed(append, 50, stream)
+    b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+    b_chunk = append_bytes(shape.batch * shape.chunk, shape.num_kv_heads, shape.bits)
+    row = _line(workload="OScaR INT2 shape, 32 x 16384 tokens, 28/4 heads, chunked prefill of 512 tokens",
+                batch=shape.batch, chunk_appends=len(full), chunk_append_ms_median=round(float(np.median(full)), 5),
+                chunk_append_GBps=round(b_chunk / float(np.median(full)) / 1e6, 1), attention_ms=round(t_att, 5),
+                attention_GBps=round(b_att / t_att / 1e6, 1), decode_token_append_ms=round(t_app, 5),
+                tokens_per_s=round(shape.batch / ((t_att + t_app) * 1e-3), 1))
+    if cpu:
+        row["cpu_oracle"] = _cpu_decode_sample(shape, n_seq=1)
+    return [row]
+
+
+def suite_tiny(dev, stream, cpu):
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("tiny")
+    plan = W.plan_pages(shape, extra_tokens=1)
+    seq, pos = W.prefill_order(shape)
+    slots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, seq, pos)).to(dev)
+    k, v = W.draw_kv_device(shape, len(seq), dev)
+    cache = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+    t_pre = _timed(lambda i: kvq.rotate_quantize_append(k, v, slots, cache, shape.hadamard_block, 0, stream=stream),
+                   50, stream)
+    append, attend, lens = _decode_step_fns(shape, plan, [cache], dev, stream)
+    t_step = _timed(lambda i: (append(i), attend(i)), 50, stream)
+    return [_line(workload="tiny: 1 x 512 tokens, 8/8 heads, Hadamard block 32 (latency)", prefill_append_ms=round(t_pre, 5),
+                  decode_step_ms=round(t_step, 5))]
+
+
+def _cpu_decode_sample(shape, n_seq):
+    """The oracle's decode of the first n_seq sequences (host inputs, a small page plan)."""
+    from oracle import kvq_oracle as O
+    from paged_decode_attention_amd import workloads as W
+    s = shape.with_(batch=n_seq, context_lens=tuple(shape.context_lens[:n_seq]))
+    plan = W.plan_pages(s, extra_tokens=0)
+    seq, pos = W.prefill_order(s)
+    k, v = W.draw_kv(s, len(seq))
+    cache = O.PagedCache(plan.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.bits)
+    O.append(cache, k, v, W.slots_for_positions(plan, s.page_size, seq, pos), s.hadamard_block, s.token_scale)
+    q = W.draw_q(s)
+    t0 = time.perf_counter()
+    O.decode(cache, q, plan.block_table, np.asarray(s.context_lens), s.num_kv_heads, s.hadamard_block)
+    dt = time.perf_counter() - t0
+    nb = decode_bytes(np.asarray(s.context_lens), s.num_q_heads, s.num_kv_heads, s.bits, s.page_size)
+    return {"kind": "oracle", "cores": len(os.sched_getaffinity(0)), "sample": f"decode of {n_seq} sequence(s)",
+            "seconds_per_seq": round(dt / n_seq, 3), "GBps": round(nb / dt / 1e9, 4)}
+
+
+def run_suite(args):
+    import torch
+    from paged_decode_attention_amd import kvq
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for fn in (suite_tiny, suite_sweep, suite_llama2_70b, suite_oscar):
+        new = fn(dev, stream, args.suite_cpu)
+        for r in new:
+            print(json.dumps(r), flush=True)
+        rows += new
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse_args()
     if args.summarize_counters:
@@ -236,6 +477,9 @@ def main():
         print(summarize_kernel_stats(args.summarize_kernel_stats, cmd))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.suite:
+        run_suite(args)
+        return
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and this build has "
               "no multi-GPU path (see the sharding paragraph of the design notes); use --gpus 1.", file=sys.stderr)

@@ -373,8 +373,12 @@ __device__ __forceinline__ void process_tile(const AppendArgs& a, int64_t tile0,
 // Items are numbered head-fastest (w = tile * H + h), so the waves that run together read the
 // same tokens' rows of all heads (one contiguous stretch of the K/V inputs) and write the
 // neighbouring page-head tiles of the cache.
+#ifndef KVQ_APPEND_MIN_WAVES
+#define KVQ_APPEND_MIN_WAVES 1   // waves per SIMD the register allocation must allow
+#endif
+
 template <int BITS, bool TOKEN_SCALE, int LB>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a, int64_t num_tiles) {
+__global__ __launch_bounds__(256, KVQ_APPEND_MIN_WAVES) void append_kernel(const AppendArgs a, int64_t num_tiles) {
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
   const int c = lane & 15;

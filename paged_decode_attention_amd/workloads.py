@@ -258,3 +258,39 @@ def shuffled_slot_mapping(rng_seed: int, n: int, num_slots: int) -> np.ndarray:
     """``n`` distinct random slots out of ``num_slots`` (for placement tests)."""
     rng = np.random.Generator(np.random.PCG64(rng_seed))
     return rng.choice(num_slots, n, replace=False).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------- device draws
+
+def draw_kv_device(shape: Shape, n_tokens: int, device, layer: int = 0, stream: str = "prefill"):
+    """Same recipe as ``draw_kv`` (N(0, 1) entries, the workload's outlier channels scaled,
+    per-token LogNormal(0, sigma) factors drawn separately for K and V, bf16 rounding), drawn
+    with torch's generator on ``device``: for timing runs whose inputs are too large to draw on
+    the host. The values differ from ``draw_kv``'s (another generator); the distribution is the
+    same. Returns two bf16 tensors [n_tokens, num_kv_heads, head_dim]."""
+    import torch
+
+    seed = (shape.seed * 1_000_003 + layer * 7919 + (0 if stream == "prefill" else 104729)) % (2 ** 63)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    ch = torch.as_tensor(outlier_channels(shape), device=device, dtype=torch.long)
+    out = []
+    for _ in range(2):
+        x = torch.randn((n_tokens, shape.num_kv_heads, shape.head_dim), generator=g, device=device,
+                        dtype=torch.float32)
+        if ch.numel():
+            x[:, :, ch] *= shape.outlier_scale
+        f = torch.empty(n_tokens, device=device, dtype=torch.float32).log_normal_(0.0, shape.lognorm_sigma, generator=g)
+        x *= f[:, None, None]
+        out.append(x.to(torch.bfloat16))
+    return out[0], out[1]
+
+
+def draw_q_device(shape: Shape, device, layer: int = 0):
+    """Decode queries drawn on ``device`` (N(0, 1), bf16), [batch, num_q_heads, head_dim]."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((shape.seed * 1_000_003 + layer * 7919 + 31) % (2 ** 63))
+    return torch.randn((shape.batch, shape.num_q_heads, shape.head_dim), generator=g, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
