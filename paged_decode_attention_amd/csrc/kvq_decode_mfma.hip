@@ -12,7 +12,7 @@
 // QK^T  (v_mfma_i32_16x16x64_i8): A = K codes of one tile (row = token, lane (G, t) holds 32
 //   channels of token t as bytes), B = the query of the group's heads as a 21-bit fixed-point
 //   integer split into three signed int8 limbs (column = head). The three limb products are
-//   combined by Horner's rule (x 128 between limbs) in exact int32 arithmetic; the output lane
+//   combined by Horner's rule (x 256 between limbs) in exact int32 arithmetic; the output lane
 //   (G, n) holds heads n, tokens 4G..4G+3.
 // PV    (v_mfma_f32_16x16x32_bf16): A = p_j delta_j for head n and tokens 4G..4G+3 of both tiles -
 //   already in the lanes the QK output left them in - split into bf16 hi + lo parts (two MFMAs);
@@ -35,6 +35,9 @@
 #endif
 #ifndef KVQ_DECODE_MIN_WAVES
 #define KVQ_DECODE_MIN_WAVES 2    // waves per SIMD the register allocation must allow
+#endif
+#ifndef KVQ_DECODE_PREFETCH_STEPS
+#define KVQ_DECODE_PREFETCH_STEPS 2  // steps of tiles loading while one is processed (2 or 3)
 #endif
 
 namespace kvq {
@@ -310,7 +313,10 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   }
   wave_lds_sync();
 
-  // ---- query as 21-bit fixed point x = rint(q' 2^E), |x| <= 2^20, in three int8 limbs
+  // ---- query as 21-bit fixed point x = rint(q' 2^E), |x| <= 2^20, in three int8 limbs: with the
+  // offset x + 0x808080 (in [0x708080, 0x908080]) its three bytes b_i are x's base-256 digits
+  // shifted by 128, so limb l_i = b_i - 128 is byte b_i with the top bit flipped, and
+  // x = (l2 * 256 + l1) * 256 + l0.
   float qv[32];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -326,30 +332,34 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   int e2 = 0;
   (void)frexpf(amax, &e2);
   const int E = (amax > 0.f) ? 20 - e2 : 0;
+  const float two_e = ldexpf(1.0f, E);  // exact: |q' 2^E| < 2^20
+  // RN(v + 1.5 * 2^23) holds rint(v) in its low mantissa bits (|v| < 2^22, ties to even)
+  constexpr float kRoundMagic = 12582912.0f;
+  constexpr uint32_t kOffsetBits = 0x4B400000u - 0x808080u;  // bits(magic + x) - this = x + 0x808080
   v4i L0[2], L1[2], L2[2];
-  int sx = 0;
+  uint32_t sxb = 0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      uint32_t d0 = 0, d1 = 0, d2 = 0;
+      uint32_t xb[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int x = static_cast<int>(rintf(ldexpf(qv[(j * 4 + r) * 4 + k], E)));
-        sx += x;
-        const int l2 = ((x + 64) & 127) - 64;
-        const int x1 = (x - l2) >> 7;
-        const int l1 = ((x1 + 64) & 127) - 64;
-        const int l0 = (x1 - l1) >> 7;
-        d0 |= (static_cast<uint32_t>(l0) & 0xFFu) << (8 * k);
-        d1 |= (static_cast<uint32_t>(l1) & 0xFFu) << (8 * k);
-        d2 |= (static_cast<uint32_t>(l2) & 0xFFu) << (8 * k);
+        xb[k] = __float_as_uint(__builtin_fmaf(qv[(j * 4 + r) * 4 + k], two_e, kRoundMagic)) - kOffsetBits;
+        sxb += xb[k];
       }
-      L0[j][r] = static_cast<int>(d0);
-      L1[j][r] = static_cast<int>(d1);
-      L2[j][r] = static_cast<int>(d2);
+      // byte i of the four values -> one dword per limb (byte k = value k), top bits flipped
+      const uint32_t lo01 = __builtin_amdgcn_perm(xb[1], xb[0], 0x05010400u);  // b0(x0) b0(x1) b1(x0) b1(x1)
+      const uint32_t lo23 = __builtin_amdgcn_perm(xb[3], xb[2], 0x05010400u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(xb[1], xb[0], 0x07030602u);  // b2(x0) b2(x1) b3 b3
+      const uint32_t hi23 = __builtin_amdgcn_perm(xb[3], xb[2], 0x07030602u);
+      L0[j][r] = static_cast<int>(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u) ^ 0x80808080u);
+      L1[j][r] = static_cast<int>(__builtin_amdgcn_perm(lo23, lo01, 0x07060302u) ^ 0x80808080u);
+      L2[j][r] = static_cast<int>(__builtin_amdgcn_perm(hi23, hi01, 0x05040100u) ^ 0x80808080u);
     }
   }
+  // sum of x over this lane's 32 values, then over the four row groups (128 channels)
+  int sx = static_cast<int>(sxb - 32u * 0x808080u);
   sx += __shfl_xor(sx, 16, 64);
   sx += __shfl_xor(sx, 32, 64);
   const float inv_scale = ldexpf(1.0f, -E);     // q' = x 2^-E
@@ -362,7 +372,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     constexpr bool full = decltype(full_tag)::value;
 
     // QK^T for the step's tiles: one exact int32 dot product per query limb (three independent
-    // MFMA chains of depth two), then x = ((s0 * 128) + s1) * 128 + s2 - Horner's rule on the
+    // MFMA chains of depth two), then x = ((s2 * 256) + s1) * 256 + s0 - Horner's rule on the
     // finished products, every partial sum below 2^31.
     v4i sc[NT];
     {
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
         s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L2[1], s2[u], 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < NT; ++u) sc[u] = (((s0[u] << 7) + s1[u]) << 7) + s2[u];
+      for (int u = 0; u < NT; ++u) sc[u] = (((s2[u] << 8) + s1[u]) << 8) + s0[u];
     }
 
     // raw scores t = delta (q~.c) + z sum(q~), in units of 2^E * log2; tokens 4G+i of tile u
@@ -482,6 +492,26 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 #pragma unroll
   for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[0][u])[lane] = x0[u].sz;
   wave_lds_sync();
+#if KVQ_DECODE_PREFETCH_STEPS == 3
+  // four buffers: while one step is processed the next three are loading
+  TileCodes x3[NT];
+  int64_t pg3[NT];
+  fetch(tile_begin + 2 * NT, x2, pg2);
+  for (int tile = tile_begin;; tile += 4 * NT) {
+    fetch(tile + 3 * NT, x3, pg3);
+    step(x0, pg0, tile, x1, 0);
+    if (tile + NT >= tile_end) break;
+    fetch(tile + 4 * NT, x0, pg0);
+    step(x1, pg1, tile + NT, x2, 1);
+    if (tile + 2 * NT >= tile_end) break;
+    fetch(tile + 5 * NT, x1, pg1);
+    step(x2, pg2, tile + 2 * NT, x3, 0);
+    if (tile + 3 * NT >= tile_end) break;
+    fetch(tile + 6 * NT, x2, pg2);
+    step(x3, pg3, tile + 3 * NT, x0, 1);
+    if (tile + 4 * NT >= tile_end) break;
+  }
+#else
   for (int tile = tile_begin;; tile += 6 * NT) {
     fetch(tile + 2 * NT, x2, pg2);
     step(x0, pg0, tile, x1, 0);
@@ -502,6 +532,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     step(x2, pg2, tile + 5 * NT, x0, 1);
     if (tile + 6 * NT >= tile_end) break;
   }
+#endif
 
   // ---- finish: totals of head n, then moved to the accumulator rows (heads 4G+i)
   l_part += __shfl_xor(l_part, 16, 64);
