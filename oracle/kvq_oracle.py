@@ -19,6 +19,10 @@ It is the plain definition of what the method computes, written out slowly with 
   matrix, scores are softmax(q k / sqrt(D)), and one inverse rotation on the output undoes
   the rotation of V.
 
+* Baseline -- attention over an unquantized bf16 paged cache (``PagedCacheBF16``,
+  ``append_bf16``, ``decode_bf16``): the BF16 split decode the OScaR abstract (thelatestinai.com
+  page) measures its speed-up against, used to put the low-bit path's speed next to it.
+
 Precision: the rotation's +-1 sums are formed exactly (float64, which holds every sum of
 at most 128 bf16 values here) and rounded once to float32, then multiplied by the float32
 constant 1/sqrt(b); the quantizer runs in float32 with IEEE division and round-half-to-
@@ -59,6 +63,7 @@ __all__ = [
     "hadamard", "rotation_matrix", "rotate_f32", "token_rms", "quantize_rows",
     "rotate_quantize", "pack_rows", "unpack_rows", "PagedCache", "append",
     "gather_sequence", "attend", "decode", "dequant_page", "bf16_to_f32",
+    "PagedCacheBF16", "append_bf16", "decode_bf16",
 ]
 
 
@@ -320,4 +325,62 @@ def dequant_page(cache: PagedCache, page: int, hadamard_block: int, unrotate: in
             if unrotate:
                 x = r.T @ x
             out[h, off] = x.astype(np.float32)
+    return out
+
+
+# ----------------------------------------------------------------------------- bf16 baseline
+
+class PagedCacheBF16:
+    """Unquantized bf16 paged cache of the baseline decode (the kind of cache a BF16 split
+    decode such as FlashDecoding-v2, the OScaR abstract's point of comparison, reads):
+
+      K  uint16 (bf16 bits) [num_pages][kv_heads][page_size][head_dim]          token-major rows
+      V  uint16 (bf16 bits) [num_pages][kv_heads][page_size / 16][head_dim][16]  channel-major
+         inside each run of 16 tokens: V of token t, channel c at [.., t // 16, c, t % 16]
+    """
+
+    def __init__(self, num_pages, kv_heads, page_size, head_dim, poison=True):
+        self.num_pages, self.kv_heads, self.page_size, self.head_dim = num_pages, kv_heads, page_size, head_dim
+        fill = 0x7FC0 if poison else 0  # bf16 NaN
+        self.k = np.full((num_pages, kv_heads, page_size, head_dim), fill, dtype=np.uint16)
+        self.v = np.full((num_pages, kv_heads, page_size // 16, head_dim, 16), fill, dtype=np.uint16)
+
+    def write_token(self, page, off, head, k_row, v_row):
+        self.k[page, head, off, :] = k_row
+        self.v[page, head, off // 16, :, off % 16] = v_row
+
+    def read_token(self, page, off, head):
+        return self.k[page, head, off, :], self.v[page, head, off // 16, :, off % 16]
+
+
+def append_bf16(cache: PagedCacheBF16, k_bits: np.ndarray, v_bits: np.ndarray, slot_mapping: np.ndarray) -> None:
+    """Copy bf16 K/V [T, H, d] to their slots unchanged (negative or out-of-pool slots skipped)."""
+    ps = cache.page_size
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0 or slot >= cache.num_pages * ps:
+            continue
+        for h in range(cache.kv_heads):
+            cache.write_token(int(slot // ps), int(slot % ps), h, k_bits[t, h], v_bits[t, h])
+
+
+def decode_bf16(cache: PagedCacheBF16, q_bits: np.ndarray, block_table: np.ndarray, context_lens: np.ndarray,
+                num_kv_heads: int, softmax_scale: float = 0.0, heads=None) -> np.ndarray:
+    """Paged decode attention over the bf16 cache (no rotation, no quantization): float32
+    [B, Hq, d]; query head h reads KV head h // (Hq / H_kv); a sequence of length 0 gives zeros."""
+    bsz, hq, d = q_bits.shape
+    g = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(d)
+    ps = cache.page_size
+    out = np.full((bsz, hq, d), np.nan, dtype=np.float32)
+    todo = heads if heads is not None else [(b, h) for b in range(bsz) for h in range(hq)]
+    for b, h in todo:
+        kvh = h // g
+        n = int(context_lens[b])
+        ks = np.zeros((n, d), dtype=np.float64)
+        vs = np.zeros((n, d), dtype=np.float64)
+        for j in range(n):
+            kr, vr = cache.read_token(int(block_table[b, j // ps]), j % ps, kvh)
+            ks[j] = bf16_to_f32(kr)
+            vs[j] = bf16_to_f32(vr)
+        out[b, h] = attend(bf16_to_f32(q_bits[b, h]), ks, vs, scale).astype(np.float32)
     return out

@@ -456,4 +456,70 @@ def pin_decode_quantization_error_small():
     assert errs[128] < errs[1]
 
 
+# ----------------------------------------------------------------------------- bf16 baseline
+
+def pin_bf16_cache_layout():
+    """Every token lands at the documented flat offsets: K at ((p*H + h)*ps + off)*d + c, V at
+    (((p*H + h)*(ps/16) + off//16)*d + c)*16 + off%16; unwritten entries keep the poison; a
+    negative slot is skipped."""
+    ps, hkv, d, npages = 32, 2, 128, 3
+    cache = O.PagedCacheBF16(npages, hkv, ps, d)
+    rng = np.random.default_rng(21)
+    slots = np.array([0, 5, 17, 31, 40, 95, -1], dtype=np.int64)
+    k = rng.integers(0, 0x7F00, size=(len(slots), hkv, d)).astype(np.uint16)
+    v = rng.integers(0, 0x7F00, size=(len(slots), hkv, d)).astype(np.uint16)
+    O.append_bf16(cache, k, v, slots)
+    kf, vf = cache.k.reshape(-1), cache.v.reshape(-1)
+    written_k = np.zeros(kf.size, bool)
+    written_v = np.zeros(vf.size, bool)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        p, off = divmod(int(slot), ps)
+        for h in range(hkv):
+            for c in range(d):
+                ik = ((p * hkv + h) * ps + off) * d + c
+                iv = (((p * hkv + h) * (ps // 16) + off // 16) * d + c) * 16 + off % 16
+                assert kf[ik] == k[t, h, c] and vf[iv] == v[t, h, c]
+                written_k[ik] = written_v[iv] = True
+    assert np.all(kf[~written_k] == 0x7FC0) and np.all(vf[~written_v] == 0x7FC0)
+
+
+def pin_decode_bf16_definition():
+    """The bf16 baseline decode is softmax(q K^T / sqrt(d)) V over the gathered rows: equal to torch's
+    scaled_dot_product_attention on the same (bf16-widened) tensors, to a brute-force loop on a
+    tiny case, independent of the page table, zero for an empty sequence, and GQA maps query
+    head h to KV head h // g."""
+    import torch
+    shape = _small_shape(hq=4, hkv=2, lens=(45, 3, 0))
+    seq, pos = W.prefill_order(shape)
+    k, v = W.draw_kv(shape, len(seq))
+    q = W.draw_q(shape)
+    lens = np.array(shape.context_lens)
+    outs = []
+    for plan in (W.identity_pages(shape, 0), W.plan_pages(shape, 0)):
+        cache = O.PagedCacheBF16(plan.num_pages, 2, 16, 128)
+        O.append_bf16(cache, k, v, W.slots_for_positions(plan, 16, seq, pos))
+        outs.append(O.decode_bf16(cache, q, plan.block_table, lens, 2))
+    assert np.array_equal(outs[0], outs[1])
+    out = outs[0]
+    assert np.all(out[2] == 0)
+    kf = O.bf16_to_f32(k).astype(np.float64)
+    vf = O.bf16_to_f32(v).astype(np.float64)
+    start = 0
+    for b, n in enumerate(shape.context_lens):
+        if n == 0:
+            continue
+        for h in range(4):
+            qq = torch.from_numpy(O.bf16_to_f32(q[b, h]).astype(np.float64))[None, None, None]
+            kk = torch.from_numpy(kf[start:start + n, h // 2])[None, None]
+            vv = torch.from_numpy(vf[start:start + n, h // 2])[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[0, 0, 0].numpy()
+            assert np.allclose(out[b, h], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max()), (b, h)
+        start += n
+    # brute force on the 3-token sequence, one head
+    bf = _brute_softmax_attention(O.bf16_to_f32(q[1, 3]), kf[45:48, 1], vf[45:48, 1], 1 / math.sqrt(128))
+    assert np.allclose(out[1, 3], bf, rtol=1e-5, atol=1e-7)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

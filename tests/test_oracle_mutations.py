@@ -170,9 +170,33 @@ def m_rms_max_abs(mp):
     mp.setattr(O, "token_rms", bad)
 
 
+def m_bf16_v_token_major(mp):
+    def write_token(self, page, off, head, k_row, v_row):
+        self.k[page, head, off, :] = k_row
+        self.v.reshape(self.num_pages, self.kv_heads, self.page_size, self.head_dim)[page, head, off, :] = v_row
+
+    def read_token(self, page, off, head):
+        return (self.k[page, head, off, :],
+                self.v.reshape(self.num_pages, self.kv_heads, self.page_size, self.head_dim)[page, head, off, :])
+    mp.setattr(O.PagedCacheBF16, "write_token", write_token)
+    mp.setattr(O.PagedCacheBF16, "read_token", read_token)
+
+
+def m_bf16_gqa_modulo(mp):
+    real = O.decode_bf16
+
+    def bad(cache, q_bits, block_table, context_lens, num_kv_heads, softmax_scale=0.0, heads=None):
+        hq = q_bits.shape[1]
+        g = hq // num_kv_heads
+        perm = np.array([(h % num_kv_heads) * g + (h // num_kv_heads) for h in range(hq)]) if g > 1 else np.arange(hq)
+        out = real(cache, q_bits[:, perm], block_table, context_lens, num_kv_heads, softmax_scale)
+        return out[:, np.argsort(perm)]
+    mp.setattr(O, "decode_bf16", bad)
+
+
 MUTATIONS = [m_hadamard_sign, m_hadamard_row_order, m_rotation_norm, m_round_half_up, m_qmax_off_by_one,
              m_zero_is_max, m_pack_high_first, m_v_interleave_swapped, m_no_softmax_scale,
-             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs]
+             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
