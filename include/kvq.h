@@ -174,6 +174,38 @@ kvq_status kvq_dequant_page(
     int32_t hadamard_block, int32_t bits, int32_t unrotate,
     float* out, hipStream_t stream);
 
+/*
+ * Baseline (for measurements side by side with the low-bit path): an unquantized bf16 paged
+ * cache and split decode attention over it - the kind of BF16 split decode (FlashDecoding-v2,
+ * named in the OScaR abstract on the thelatestinai.com page) the pages compare their speed-ups
+ * against. Same block table, context lengths, GQA rule, softmax scale, workspace (size from
+ * kvq_paged_decode_workspace_size with the same arguments) and error behaviour as
+ * kvq_paged_decode_attention; no rotation.
+ *
+ * Cache layout (bf16 bit patterns, caller-owned device memory):
+ *   k_cache  uint16 [num_pages][num_kv_heads][page_size][head_dim]            token-major rows
+ *   v_cache  uint16 [num_pages][num_kv_heads][page_size / 16][head_dim][16]   channel-major inside
+ *            each run of 16 tokens: token t, channel c at [.., t / 16, c, t % 16]
+ */
+
+/* Copy bf16 K/V [num_tokens][num_kv_heads][head_dim] (token strides as for
+ * kvq_rotate_quantize_append) to their slots; negative or out-of-pool slots are skipped. */
+kvq_status kvq_bf16_cache_write(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+    const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+    int32_t num_pages, int32_t page_size, hipStream_t stream);
+
+/* Decode attention over the bf16 cache: out float32 [batch][num_q_heads][head_dim];
+ * at most 16 query heads per KV head. */
+kvq_status kvq_paged_decode_attention_bf16(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

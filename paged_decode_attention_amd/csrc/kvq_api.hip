@@ -289,4 +289,85 @@ kvq_status kvq_dequant_page(
   return kvq::launch_dequant(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+
+// ---------------------------------------------------------------------------- bf16 baseline
+
+kvq_status kvq_bf16_cache_write(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+    const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
+    int32_t num_pages, int32_t page_size, hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_pages < 0 || page_size <= 0) return KVQ_ERR_SHAPE;
+  if (head_dim != kvq::kHeadDim || page_size % kvq::kTileTokens) return KVQ_ERR_UNSUPPORTED;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (k_token_stride < row_elems || v_token_stride < row_elems || k_token_stride % 8 || v_token_stride % 8)
+    return KVQ_ERR_SHAPE;
+  if (num_kv_heads > 65535 || (num_tokens + 15) / 16 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return KVQ_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16))
+    return KVQ_ERR_SHAPE;
+  kvq::Bf16WriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_slots = static_cast<int64_t>(num_pages) * page_size;
+  a.page_size = page_size;
+  return kvq::launch_bf16_write(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_paged_decode_attention_bf16(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
+      max_pages_per_seq < 0 || pages_per_split < 0 || page_size <= 0)
+    return KVQ_ERR_SHAPE;
+  if (head_dim != kvq::kHeadDim || page_size % kvq::kTileTokens) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % num_kv_heads) return KVQ_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 16) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
+  if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return KVQ_ERR_SHAPE;
+  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
+  kvq::DecodeBf16Args a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_size = page_size;
+  a.block_table = block_table;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_pages = num_pages;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
+  a.qk_scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  a.out = out;
+  a.num_splits = plan.num_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ws_acc = ws.total ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
+  return kvq::launch_decode_bf16(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
 }  // extern "C"

@@ -671,6 +671,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
+  return launch_decode_merge(a, stream);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
   hipLaunchKernelGGL(decode_merge_splits_kernel, dim3(static_cast<unsigned>(pairs)), dim3(64), 0, stream, a);
   return hipGetLastError();

@@ -88,7 +88,46 @@ struct DequantArgs {
   float* out;
 };
 
+// Baseline: unquantized bf16 paged cache (K token-major, V channel-major per 16 tokens).
+struct Bf16WriteArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_stride, v_stride;     // elements between tokens
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  const int64_t* slots;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t num_slots;
+  int32_t page_size;
+};
+
+struct DecodeBf16Args {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  int32_t page_size;
+  const int32_t* block_table;
+  int32_t max_pages_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  int32_t num_pages;
+  int32_t batch, num_q_heads, num_kv_heads;
+  float qk_scale_log2;            // softmax_scale * log2(e)
+  float* out;
+  int32_t num_splits;
+  int32_t pages_per_split;
+  float* ws_acc;                  // same layout as DecodeArgs
+  float* ws_ml;
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_bf16_write(const Bf16WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeBf16Args& a, hipStream_t stream);
+// Log-sum-exp merge of the split partials (ws_acc, ws_ml) into out, then the inverse rotation
+// given by a.rot (the identity plan for block size 1); reads a.context_lens, a.max_context_len,
+// a.page_size, a.pages_per_split, a.num_splits, a.batch, a.num_q_heads.
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

@@ -18,7 +18,8 @@ HEAD_DIM = 128
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = range(6)
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
-           "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page")
+           "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page",
+           "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16")
 
 
 class KVQError(RuntimeError):
@@ -55,6 +56,11 @@ def lib() -> ctypes.CDLL:
         _p, _p, _sz, _i32, _p]
     L.kvq_dequant_page.restype = _i32
     L.kvq_dequant_page.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
+    L.kvq_bf16_cache_write.restype = _i32
+    L.kvq_bf16_cache_write.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _p]
+    L.kvq_paged_decode_attention_bf16.restype = _i32
+    L.kvq_paged_decode_attention_bf16.argtypes = [
+        _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz, _i32, _p]
     _lib = L
     return L
 
@@ -220,4 +226,87 @@ def dequant_page(cache: PagedKVCache, tensor: str, page: int, hadamard_block: in
                                 cache.page_size, HEAD_DIM, hadamard_block, cache.bits, unrotate,
                                 _dev(out, "out", torch.float32), _stream(stream))
     _check(st, "kvq_dequant_page")
+    return out
+
+
+# ----------------------------------------------------------------------------- bf16 baseline
+
+@dataclass
+class PagedKVCacheBF16:
+    """Unquantized bf16 cache of the baseline decode (two device tensors of bf16)."""
+    k: torch.Tensor   # bfloat16 [P, H, ps, 128]
+    v: torch.Tensor   # bfloat16 [P, H, ps/16, 128, 16]
+
+    @staticmethod
+    def empty(num_pages: int, num_kv_heads: int, page_size: int, device="cuda") -> "PagedKVCacheBF16":
+        return PagedKVCacheBF16(
+            torch.empty((num_pages, num_kv_heads, page_size, HEAD_DIM), dtype=torch.bfloat16, device=device),
+            torch.empty((num_pages, num_kv_heads, page_size // 16, HEAD_DIM, 16), dtype=torch.bfloat16, device=device))
+
+    @property
+    def num_pages(self) -> int:
+        return self.k.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k.shape[1]
+
+    @property
+    def page_size(self) -> int:
+        return self.k.shape[2]
+
+    def _check_layout(self):
+        p, h, ps, d = self.k.shape
+        if d != HEAD_DIM or tuple(self.v.shape) != (p, h, ps // 16, HEAD_DIM, 16):
+            raise ValueError("bf16 cache tensors do not match the documented layout")
+        if not (self.k.is_contiguous() and self.v.is_contiguous()):
+            raise ValueError("cache tensors must be contiguous")
+
+
+def bf16_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, cache: PagedKVCacheBF16,
+                     stream=None) -> None:
+    """kvq_bf16_cache_write on bf16 k, v [T, H, 128] (contiguous heads) and int64 slots [T]."""
+    cache._check_layout()
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or t.shape[1] != cache.num_kv_heads or t.shape[2] != HEAD_DIM or t.stride(2) != 1 \
+                or t.stride(1) != HEAD_DIM:
+            raise ValueError(f"{name} must be [T, {cache.num_kv_heads}, {HEAD_DIM}] with contiguous heads")
+    if k.shape[0] != v.shape[0] or slot_mapping.shape != (k.shape[0],) or not slot_mapping.is_contiguous():
+        raise ValueError("k, v and slot_mapping disagree on the number of tokens")
+    st = lib().kvq_bf16_cache_write(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16), k.stride(0), v.stride(0), k.shape[0],
+        cache.num_kv_heads, HEAD_DIM, _dev(slot_mapping, "slot_mapping", torch.int64),
+        _dev(cache.k, "k_cache", torch.bfloat16), _dev(cache.v, "v_cache", torch.bfloat16), cache.num_pages,
+        cache.page_size, _stream(stream))
+    _check(st, "kvq_bf16_cache_write")
+
+
+def paged_decode_attention_bf16(q: torch.Tensor, cache: PagedKVCacheBF16, block_table: torch.Tensor,
+                                context_lens: torch.Tensor, max_context_len: int, softmax_scale: float = 0.0,
+                                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                                pages_per_split: int = 0, stream=None) -> torch.Tensor:
+    """kvq_paged_decode_attention_bf16: q bf16 [B, Hq, 128] -> float32 [B, Hq, 128]."""
+    cache._check_layout()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    bsz, hq, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] int32 tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+    if out is None:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (bsz, hq, HEAD_DIM) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
+    need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().kvq_paged_decode_attention_bf16(
+        _dev(q, "q", torch.bfloat16), _dev(cache.k, "k_cache", torch.bfloat16), _dev(cache.v, "v_cache", torch.bfloat16),
+        cache.num_pages, cache.page_size, _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, bsz, hq, cache.num_kv_heads, HEAD_DIM,
+        float(softmax_scale), _dev(out, "out", torch.float32), ws_ptr, ws_bytes, pages_per_split, _stream(stream))
+    _check(st, "kvq_paged_decode_attention_bf16")
     return out

@@ -143,3 +143,24 @@ def test_binding_refuses_host_tensors():
     c = kvq.PagedKVCache.empty(4, 2, 16, 4, device="cpu")
     with pytest.raises(ValueError):
         kvq.dequant_page(c, "k", 0, 32)
+
+
+def test_bf16_baseline_validation():
+    L = kvq.lib()
+    w = lambda **kw: L.kvq_bf16_cache_write(NULL, NULL, kw.get("ks", 1024), 1024, kw.get("n", 4), 8, kw.get("d", 128),
+                                            NULL, NULL, NULL, 10, kw.get("ps", 16), NULL)
+    assert w() == kvq.KVQ_ERR_NULL
+    assert w(n=0) == kvq.KVQ_OK
+    assert w(d=64) == kvq.KVQ_ERR_UNSUPPORTED
+    assert w(ps=24) == kvq.KVQ_ERR_UNSUPPORTED
+    assert w(ks=1000) == kvq.KVQ_ERR_SHAPE
+
+    def dec(**kw):
+        return L.kvq_paged_decode_attention_bf16(
+            NULL, NULL, NULL, 10, 16, NULL, kw.get("mp", 4), NULL, kw.get("ml", 64), kw.get("b", 2),
+            kw.get("hq", 32), kw.get("hkv", 8), 128, 0.0, NULL, NULL, 0, 0, NULL)
+    assert dec() == kvq.KVQ_ERR_NULL
+    assert dec(b=0) == kvq.KVQ_OK
+    assert dec(hq=30) == kvq.KVQ_ERR_SHAPE            # not a multiple of the KV heads
+    assert dec(hq=136) == kvq.KVQ_ERR_UNSUPPORTED     # 17 query heads per KV head
+    assert dec(mp=3) == kvq.KVQ_ERR_SHAPE             # block table too narrow for 64 tokens
