@@ -290,6 +290,49 @@ def _decode_step_fns(shape, plan, caches, dev, stream, layer=0):
     return append, attend, lens
 
 
+def _bf16_attention(shape, plan, dev, stream, n_copies=None, layer=0):
+    """Average ms (and GB/s) of the bf16 baseline decode over caches holding the same synthetic
+    sequences as the low-bit run: the prefill plus the decode step's new token."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    cache_bytes = plan.num_pages * shape.num_kv_heads * shape.page_size * 128 * 2 * 2
+    if n_copies is None:
+        n_copies = int(min(16, max(1, math.ceil(1.1e9 / cache_bytes))))
+    seq, pos = W.prefill_order(shape)
+    slots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, seq, pos)).to(dev)
+    k, v = W.draw_kv_device(shape, len(seq), dev, layer=layer)
+    dseq, dpos = W.decode_positions(shape)
+    dslots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, dseq, dpos)).to(dev)
+    kn, vn = W.draw_kv_device(shape, shape.batch, dev, layer=layer, stream="decode")
+    lens = np.asarray(shape.context_lens, dtype=np.int64) + 1
+    caches = []
+    for _ in range(n_copies):
+        c = kvq.PagedKVCacheBF16.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, device=dev)
+        kvq.bf16_cache_write(k, v, slots, c, stream=stream)
+        kvq.bf16_cache_write(kn, vn, dslots, c, stream=stream)
+        caches.append(c)
+    del k, v
+    q = W.draw_q_device(shape, dev, layer=layer)
+    lens_d = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(dev)
+    bt = torch.from_numpy(plan.block_table).to(dev)
+    max_len = int(np.max(lens))
+    ws = kvq.decode_workspace(kvq.decode_workspace_size(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
+                                                        shape.page_size), dev)
+    out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def attend(i):
+        kvq.paged_decode_attention_bf16(q, caches[i % n_copies], bt, lens_d, max_len, out=out, workspace=ws,
+                                        stream=stream)
+    for i in range(5):
+        attend(i)
+    ms = _timed(attend, 50, stream)
+    toks = int(np.sum(lens))
+    nbytes = toks * shape.num_kv_heads * 512 + shape.batch * shape.num_q_heads * 128 * 6
+    del caches
+    return ms, nbytes / ms / 1e6
+
+
 def _line(**kw):
     return kw
 
@@ -319,6 +362,11 @@ def suite_sweep(dev, stream, cpu):
                               step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
                               tokens_per_s=round(b / (t_step * 1e-3), 1)))
             del caches
+            if hb == 64:
+                t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream)
+                rows[-1].update(bf16_attention_ms=round(t_bf, 5), bf16_attention_GBps=round(gb_bf, 1),
+                                attention_speedup_vs_bf16=round(t_bf / t_att, 2),
+                                cache_bytes_ratio_bf16=round(512 / (2 * 128 * shape.bits // 8 + 16), 2))
             if cpu and hb == 64 and b <= 8:
                 rows[-1]["cpu_oracle"] = _cpu_decode_sample(shape, n_seq=min(b, 2))
     return rows
@@ -357,6 +405,13 @@ def suite_llama2_70b(dev, stream, cpu):
                 attention_ms_per_layer=round(t_att / shape.layers, 5), attention_GBps=round(b_att / t_att / 1e6, 1),
                 step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
                 tokens_per_s=round(shape.batch / (t_step * 1e-3), 1))
+    del layers, step, attention_only
+    torch_empty_cache()
+    plan0 = W.plan_pages(shape, extra_tokens=1)
+    t_bf, gb_bf = _bf16_attention(shape, plan0, dev, stream, n_copies=4)
+    row.update(bf16_attention_ms_per_layer=round(t_bf, 5), bf16_attention_GBps=round(gb_bf, 1),
+               attention_speedup_vs_bf16=round(t_bf / (t_att / shape.layers), 2),
+               cache_bytes_ratio_bf16=round(512 / (2 * 128 * shape.bits // 8 + 16), 2))
     if cpu:
         c = _cpu_decode_sample(shape, n_seq=1)
         c["extrapolated_step_s"] = round(c["seconds_per_seq"] * shape.batch * shape.layers, 1)
@@ -401,7 +456,13 @@ def suite_oscar(dev, stream, cpu):
     t_app = _timed(append, 50, stream)
     b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
     b_chunk = append_bytes(shape.batch * shape.chunk, shape.num_kv_heads, shape.bits)
+    del copies, cache
+    torch_empty_cache()
+    t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream)
     row = _line(workload="OScaR INT2 shape, 32 x 16384 tokens, 28/4 heads, chunked prefill of 512 tokens",
+                bf16_attention_ms=round(t_bf, 5), bf16_attention_GBps=round(gb_bf, 1),
+                attention_speedup_vs_bf16=round(t_bf / t_att, 2),
+                cache_bytes_ratio_bf16=round(512 / (2 * 128 * shape.bits // 8 + 16), 2),
                 batch=shape.batch, chunk_appends=len(full), chunk_append_ms_median=round(float(np.median(full)), 5),
                 chunk_append_GBps=round(b_chunk / float(np.median(full)) / 1e6, 1), attention_ms=round(t_att, 5),
                 attention_GBps=round(b_att / t_att / 1e6, 1), decode_token_append_ms=round(t_app, 5),
@@ -446,6 +507,12 @@ def _cpu_decode_sample(shape, n_seq):
     nb = decode_bytes(np.asarray(s.context_lens), s.num_q_heads, s.num_kv_heads, s.bits, s.page_size)
     return {"kind": "oracle", "cores": len(os.sched_getaffinity(0)), "sample": f"decode of {n_seq} sequence(s)",
             "seconds_per_seq": round(dt / n_seq, 3), "GBps": round(nb / dt / 1e9, 4)}
+
+
+def torch_empty_cache():
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def run_suite(args):
@@ -659,6 +726,13 @@ def main():
         "decode_tokens_per_s": kernels["paged_decode_attention_alone"]["decode_tokens_per_s"],
         "kernels": kernels, "roofline": roofline, "roofline_decode": roofline_decode,
     }
+    # the same decode over an unquantized bf16 cache (the baseline the pages compare against)
+    del caches
+    torch.cuda.empty_cache()
+    t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream, n_copies=4)
+    result["baseline_bf16_decode"] = {
+        "avg_ms": round(t_bf, 5), "GBps": round(gb_bf, 1), "speedup_of_int%d_decode" % shape.bits: round(t_bf / dec_avg, 2),
+        "cache_bytes_ratio": round(512 / (2 * 128 * shape.bits // 8 + 16), 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, k, v, slots, plan, q)
     print(json.dumps(result), flush=True)
