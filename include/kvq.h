@@ -164,6 +164,34 @@ kvq_status kvq_paged_decode_attention(
     hipStream_t stream);
 
 /*
+ * Fused decode step: append each sequence's new token and attend, in one launch (the fused
+ * pipeline of the OSCAR abstract on the thelatestinai.com page; one launch per layer per step).
+ * Equivalent to kvq_rotate_quantize_append of k_new[b], v_new[b] at the slot of position
+ * context_lens[b] - 1 (block_table[b][(L - 1) / page_size] * page_size + (L - 1) % page_size), followed by
+ * kvq_paged_decode_attention over context_lens[b] tokens - so the new token is attended.
+ *
+ *   k_new, v_new     bf16 [batch][num_kv_heads][head_dim], token stride k_new_stride / v_new_stride
+ *                    (elements, >= num_kv_heads * head_dim, a multiple of 8): the new token of each
+ *                    sequence. Sequences with context_lens[b] == 0 append nothing (zero output); an
+ *                    invalid page id at position L - 1 skips the append and masks the page.
+ *   token_scale      as for kvq_rotate_quantize_append.
+ *   All other arguments and the workspace as for kvq_paged_decode_attention (the cache arrays are
+ *   written, so they are not const here). Only the query heads' outputs and the new tokens' cache
+ *   rows change.
+ */
+kvq_status kvq_decode_step(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint16_t* k_new, const uint16_t* v_new, int64_t k_new_stride, int64_t v_new_stride,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_sz, float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, int32_t token_scale, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream);
+
+/*
  * Dequantize every token of one page of the K (tensor = 0) or V (tensor = 1) half of the
  * cache: out float32 [num_kv_heads][page_size][head_dim] = code * scale + zero (a single
  * rounding), multiplied by R^T when unrotate = 1. page must lie in [0, num_pages).

@@ -197,16 +197,19 @@ size_t kvq_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
   return workspace_layout(p.num_splits, batch, num_q_heads).total;
 }
 
-kvq_status kvq_paged_decode_attention(
-    const uint16_t* q, int32_t q_prerotated,
+}  // extern "C"
+
+namespace {
+
+// Validation and argument set-up shared by the decode and the fused decode step.
+kvq_status decode_args(
+    kvq::DecodeArgs& a, const uint16_t* q, int32_t q_prerotated,
     const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
-    int32_t num_pages, int32_t page_size,
-    const int32_t* block_table, int32_t max_pages_per_seq,
+    int32_t num_pages, int32_t page_size, const int32_t* block_table, int32_t max_pages_per_seq,
     const int32_t* context_lens, int32_t max_context_len,
     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t hadamard_block, int32_t bits, float softmax_scale,
-    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
-    hipStream_t stream) {
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
       max_pages_per_seq < 0 || pages_per_split < 0)
     return KVQ_ERR_SHAPE;
@@ -227,7 +230,7 @@ kvq_status kvq_paged_decode_attention(
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
 
-  kvq::DecodeArgs a{};
+  a = kvq::DecodeArgs{};
   a.q = q;
   a.q_prerotated = q_prerotated;
   a.k_codes = k_codes;
@@ -260,7 +263,71 @@ kvq_status kvq_paged_decode_attention(
   a.pages_per_split = plan.pages_per_split;
   a.ws_acc = ws.total ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_paged_decode_attention(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream) {
+  kvq::DecodeArgs a;
+  if (kvq_status s = decode_args(a, q, q_prerotated, k_codes, v_codes, k_sz, v_sz, num_pages, page_size, block_table,
+                                 max_pages_per_seq, context_lens, max_context_len, batch, num_q_heads, num_kv_heads,
+                                 head_dim, hadamard_block, bits, softmax_scale, out, workspace, workspace_bytes,
+                                 pages_per_split))
+    return s;
+  if (batch == 0) return KVQ_OK;
   return kvq::launch_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_decode_step(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint16_t* k_new, const uint16_t* v_new, int64_t k_new_stride, int64_t v_new_stride,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_sz, float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, int32_t token_scale, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream) {
+  // shape checks of the new tokens first, as every entry point checks shapes before pointers
+  if (token_scale != 0 && token_scale != 1) return KVQ_ERR_SHAPE;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (num_kv_heads > 0 && (k_new_stride < row_elems || v_new_stride < row_elems || k_new_stride % 8 ||
+                           v_new_stride % 8))
+    return KVQ_ERR_SHAPE;
+  kvq::DecodeArgs a;
+  if (kvq_status s = decode_args(a, q, q_prerotated, k_codes, v_codes, k_sz, v_sz, num_pages, page_size, block_table,
+                                 max_pages_per_seq, context_lens, max_context_len, batch, num_q_heads, num_kv_heads,
+                                 head_dim, hadamard_block, bits, softmax_scale, out, workspace, workspace_bytes,
+                                 pages_per_split))
+    return s;
+  if (batch == 0) return KVQ_OK;
+  if (!k_new || !v_new) return KVQ_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return KVQ_ERR_SHAPE;
+  a.fused = 1;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_new_stride = k_new_stride;
+  a.v_new_stride = v_new_stride;
+  a.token_scale = token_scale;
+  a.k_codes_w = k_codes;
+  a.v_codes_w = v_codes;
+  a.k_sz_w = k_sz;
+  a.v_sz_w = v_sz;
+  a.use_valu = 0;  // the fused step exists on the matrix-core kernel only
+  return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 kvq_status kvq_dequant_page(

@@ -211,6 +211,98 @@ __device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t row0
   return t;
 }
 
+// ---------------------------------------------------------------------------- fused decode step
+// Rotate, optionally scale, quantize and pack the 8 channels this lane holds of one head vector
+// (a 16-lane row group holds the vector): the write path for a single token, with the in-register
+// butterfly instead of the matrix cores. Returns the packed codes of output block lf.pos (INT4:
+// 4 bytes, INT2: 2 bytes) and the stored scale and zero (equal in the row group's 16 lanes).
+template <int BITS, bool TOKEN_SCALE>
+__device__ __forceinline__ uint32_t rotate_quantize_row(float (&x)[8], const RowFwhtPlan& rot, const LaneFwht& lf,
+                                                        float& scale, float& zero) {
+  fwht_row16_planned(x, rot, lf);
+  float s = 1.0f;
+  if constexpr (TOKEN_SCALE) {
+    double ss = 0.0;  // RMS in double precision, rounded once to float; 1 for an all-zero vector
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss += static_cast<double>(x[k]) * static_cast<double>(x[k]);
+    ss = row16_sum_f64(ss);
+    s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
+    if (s == 0.0f) s = 1.0f;
+    const float rs = 1.0f / s;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = div_rn(x[k], s, rs);
+  }
+  float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mn = row16_min(mn);
+  mx = row16_max(mx);
+  constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
+  const float delta = (mx - mn) / kQmax;  // IEEE division
+  uint32_t packed = 0;
+  if (delta != 0.0f) {
+    const float r = 1.0f / delta;
+    float c[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(rintf(div_rn(x[k] - mn, delta, r)), 0.0f), kQmax);
+    if constexpr (BITS == 4) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        packed = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * m + 1], 16.0f, c[2 * m]), m, packed);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[4 * m + 3], 4.0f, c[4 * m + 2]), 4.0f,
+                                                       c[4 * m + 1]), 4.0f, c[4 * m]);
+        packed = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, packed);
+      }
+    }
+  }
+  scale = delta * s;
+  zero = mn * s;
+  return packed;
+}
+
+// The new token of sequence b (position len - 1) for KV head kvh: row group 0 writes K, row group
+// 1 writes V (groups 2 and 3 repeat the work and store nothing). Waits until the stores are done,
+// so that this wave's later loads of the same page see them (no other wave reads this page-head
+// tile in the call).
+template <int BITS>
+__device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int kvh, int pos, int32_t page, int lane) {
+  constexpr int kRow = kHeadDim * BITS / 8;
+  constexpr int kLaneBytes = 8 * BITS / 8;
+  const int G = lane >> 4;
+  const int li = lane & 15;
+  const bool is_v = (G & 1) != 0;
+  const uint16_t* src = is_v ? a.v_new + static_cast<int64_t>(b) * a.v_new_stride
+                             : a.k_new + static_cast<int64_t>(b) * a.k_new_stride;
+  float x[8];
+  bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + kvh * kHeadDim + 8 * li), x);
+  const LaneFwht lf = lane_fwht(a.rot, li);
+  float scale, zero;
+  const uint32_t packed = a.token_scale ? rotate_quantize_row<BITS, true>(x, a.rot, lf, scale, zero)
+                                        : rotate_quantize_row<BITS, false>(x, a.rot, lf, scale, zero);
+  const int ps = a.page_size;
+  const int off = pos % ps;
+  const int64_t tile = static_cast<int64_t>(page) * a.num_kv_heads + kvh;  // (page, head) tile
+  const int64_t row = tile * ps + off;
+  if (G == 0) {
+    uint8_t* k = a.k_codes_w + row * kRow + kLaneBytes * lf.pos;
+    if constexpr (BITS == 4) {
+      *reinterpret_cast<uint32_t*>(k) = packed;
+    } else {
+      *reinterpret_cast<uint16_t*>(k) = static_cast<uint16_t>(packed);
+    }
+    if (li == 0) reinterpret_cast<float2*>(a.k_sz_w)[row] = make_float2(scale, zero);
+  } else if (G == 1) {
+    uint8_t* v = a.v_codes_w + tile * ps * kRow + ((off >> 2) * kRow + kLaneBytes * lf.pos) * 4 + (off & 3);
+#pragma unroll
+    for (int m = 0; m < kLaneBytes; ++m) v[4 * m] = static_cast<uint8_t>(packed >> (8 * m));
+    if (li == 0) reinterpret_cast<float2*>(a.v_sz_w)[row] = make_float2(scale, zero);
+  }
+  // the stores complete before any later load is issued (and the compiler moves no load above)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int BITS, bool PS16, int NT>
 __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
   __shared__ float qs[8][kHeadDim];
@@ -231,6 +323,16 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // the last split also takes the pages past num_splits * pages_per_split (see plan_splits)
   const int p_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split);
   const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g) * kHeadDim;
+
+  if (a.fused && len > 0) {
+    // this split owns the last page: write the new token first
+    const int pos = len - 1;
+    const int last_page = pos / ps;
+    if (last_page >= p_begin && last_page < p_end) {
+      const int32_t page = ro_load(a.block_table, static_cast<int64_t>(b) * a.max_pages_per_seq + last_page);
+      if (page >= 0 && page < a.num_pages) append_new_token<BITS>(a, b, kvh, pos, page, lane);
+    }
+  }
 
   if (p_begin >= p_end) {
     if (a.num_splits == 1) {  // empty sequence: zero output

@@ -72,6 +72,17 @@ struct DecodeArgs {
   int32_t pages_per_split;
   float* ws_acc;                  // [num_splits][batch][num_q_heads][128]
   float* ws_ml;                   // [num_splits][batch][num_q_heads][2]  (max, sum) in log2 units
+  // Fused decode step: before attending, the wave that owns a sequence's last page rotates,
+  // quantizes and writes that sequence's new token (position context_lens[b] - 1) for its KV head.
+  int32_t fused;
+  const uint16_t* k_new;          // bf16 [batch][num_kv_heads][128], token stride k_new_stride
+  const uint16_t* v_new;
+  int64_t k_new_stride, v_new_stride;
+  int32_t token_scale;
+  uint8_t* k_codes_w;             // the same cache as k_codes ... v_sz, writable
+  uint8_t* v_codes_w;
+  float* k_sz_w;
+  float* v_sz_w;
 };
 
 struct DequantArgs {

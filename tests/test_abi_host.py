@@ -164,3 +164,18 @@ def test_bf16_baseline_validation():
     assert dec(hq=30) == kvq.KVQ_ERR_SHAPE            # not a multiple of the KV heads
     assert dec(hq=136) == kvq.KVQ_ERR_UNSUPPORTED     # 17 query heads per KV head
     assert dec(mp=3) == kvq.KVQ_ERR_SHAPE             # block table too narrow for 64 tokens
+
+
+def test_decode_step_validation():
+    L = kvq.lib()
+
+    def step(**kw):
+        return L.kvq_decode_step(
+            NULL, 0, NULL, NULL, kw.get("ks", 1024), 1024, NULL, NULL, NULL, NULL, 10, 16, NULL, 4, NULL, 64,
+            kw.get("b", 2), 32, 8, 128, kw.get("hb", 128), kw.get("bits", 4), kw.get("ts", 0), 0.0, NULL, NULL, 0, 0,
+            NULL)
+    assert step() == kvq.KVQ_ERR_NULL
+    assert step(b=0) == kvq.KVQ_OK
+    assert step(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
+    assert step(ts=2) == kvq.KVQ_ERR_SHAPE
+    assert step(ks=1000) == kvq.KVQ_ERR_SHAPE
