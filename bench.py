@@ -5,8 +5,8 @@ One step = the whole hot path over one batch of the Llama-3-8B-shaped layer (16 
 4096 tokens, 32 query / 8 KV heads, head_dim 128, page size 16, Hadamard block 128, INT4):
 
   1. rotate-quantize-append of the 16 x 4096 prefill tokens (write path, all 8 KV heads),
-  2. rotate-quantize-append of one new decode token per sequence,
-  3. paged decode attention over 4097 tokens per sequence (read path).
+  2. the decode step: rotate-quantize-append of one new token per sequence and paged decode
+     attention over the 4097 tokens (read path), fused in one launch (kvq_decode_step).
 
 Inputs are seeded synthetic bf16 tensors resident in HBM before timing starts. To keep the
 256 MB Infinity Cache from serving reads, steps rotate over 4 copies of the prefill inputs and
@@ -287,6 +287,11 @@ def _decode_step_fns(shape, plan, caches, dev, stream, layer=0):
     def attend(i):
         kvq.paged_decode_attention(q, caches[i % len(caches)], bt, lens_d, max_len, shape.hadamard_block, out=out,
                                    workspace=ws, stream=stream)
+
+    def fused(i):
+        kvq.decode_step(q, kn, vn, caches[i % len(caches)], bt, lens_d, max_len, shape.hadamard_block,
+                        token_scale=shape.token_scale, out=out, workspace=ws, stream=stream)
+    append.fused = fused
     return append, attend, lens
 
 
@@ -393,19 +398,26 @@ def suite_llama2_70b(dev, stream, cpu):
     def attention_only(i):
         for _, attend, _ in layers:
             attend(0)
+
+    def step_fused(i):
+        for append, _, _ in layers:
+            append.fused(0)
     for i in range(2):
         step(i)
+        step_fused(i)
     t_step = _timed(step, 10, stream)
     t_att = _timed(attention_only, 10, stream)
+    t_fused = _timed(step_fused, 10, stream)
     lens = layers[0][2]
     b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size) * shape.layers
     b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits) * shape.layers
     row = _line(workload="Llama-2-70B shape, 4 x 32768 tokens, 64/8 heads, 80 layers (one step)", batch=shape.batch,
-                layers=shape.layers, step_ms=round(t_step, 4), attention_ms_80_layers=round(t_att, 4),
+                layers=shape.layers, step_ms=round(t_step, 4), fused_step_ms=round(t_fused, 4),
+                fused_tokens_per_s=round(shape.batch / (t_fused * 1e-3), 1), attention_ms_80_layers=round(t_att, 4),
                 attention_ms_per_layer=round(t_att / shape.layers, 5), attention_GBps=round(b_att / t_att / 1e6, 1),
                 step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
                 tokens_per_s=round(shape.batch / (t_step * 1e-3), 1))
-    del layers, step, attention_only
+    del layers, step, attention_only, step_fused
     torch_empty_cache()
     plan0 = W.plan_pages(shape, extra_tokens=1)
     t_bf, gb_bf = _bf16_attention(shape, plan0, dev, stream, n_copies=4)
@@ -607,6 +619,11 @@ def main():
         kvq.paged_decode_attention(q_d, caches[c % N_CACHE_COPIES], bt_d, lens_d, max_len, hb, out=out,
                                    workspace=ws, stream=stream)
 
+    def decode_step(c):
+        # one launch: append the decode token (position 4096) and attend over 4097 tokens
+        kvq.decode_step(q_d, kn_d, vn_d, caches[c % N_CACHE_COPIES], bt_d, lens_d, max_len, hb, token_scale=ts,
+                        out=out, workspace=ws, stream=stream)
+
     # every cache copy holds a full prefill + decode token before anything is timed
     for i in range(N_CACHE_COPIES):
         prefill(i)
@@ -614,17 +631,15 @@ def main():
     torch.cuda.synchronize()
 
     def step(i, ev=None):
+        # the prefill rewrites copy i; the decode step works on the copy written seven steps ago
         if ev is not None:
             ev[0].record(stream)
         prefill(i)
         if ev is not None:
             ev[1].record(stream)
-        decode_append(i)
+        decode_step(i + N_CACHE_COPIES // 2)
         if ev is not None:
             ev[2].record(stream)
-        attend(i + N_CACHE_COPIES // 2)
-        if ev is not None:
-            ev[3].record(stream)
 
     if args.counters:
         # calibration copy of known size, then the steps the counters are read on
@@ -641,7 +656,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -653,8 +668,14 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     prefill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dapp_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    attn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    dstep_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    # the same decode step as two launches (append, then attention), for comparison
+    for i in range(5):
+        decode_append(i), attend(i)
+    torch.cuda.synchronize()
+    sep_ms = _timed(lambda i: (decode_append(i), attend(i)), 50, stream)
+    fused_ms = _timed(decode_step, 50, stream)
 
     # decode attention alone, back to back, cycling over the 14 cache copies: blocks of 20
     # launches between events (so event overhead does not enter the per-launch time)
@@ -680,15 +701,20 @@ def main():
     def gbps(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
-    pre_avg, attn_avg, dec_avg = float(prefill_ms.mean()), float(attn_ms.mean()), float(dec_only_ms.mean())
+    pre_avg, dstep_avg, dec_avg = float(prefill_ms.mean()), float(dstep_ms.mean()), float(dec_only_ms.mean())
     kernels = {
         "rotate_quantize_append_prefill": {"bytes": b_prefill, "avg_ms": round(pre_avg, 5),
                                            "GBps": round(gbps(b_prefill, pre_avg), 1),
                                            "frac_of_peak": round(gbps(b_prefill, pre_avg) / PEAK_HBM_GBPS, 4),
                                            "tokens_per_s": round(len(seq) / (pre_avg * 1e-3), 1)},
-        "rotate_quantize_append_decode_token": {"bytes": b_dapp, "avg_ms": round(float(dapp_ms.mean()), 5)},
-        "paged_decode_attention_in_step": {"bytes": b_attn, "avg_ms": round(attn_avg, 5),
-                                           "GBps": round(gbps(b_attn, attn_avg), 1)},
+        "decode_step_fused_in_step": {"bytes": b_dapp + b_attn, "avg_ms": round(dstep_avg, 5),
+                                      "GBps": round(gbps(b_dapp + b_attn, dstep_avg), 1),
+                                      "note": "kvq_decode_step: decode-token append + attention in one launch"},
+        "decode_step_fused_back_to_back": {"bytes": b_dapp + b_attn, "avg_ms": round(fused_ms, 5),
+                                           "GBps": round(gbps(b_dapp + b_attn, fused_ms), 1)},
+        "decode_step_two_launches": {"bytes": b_dapp + b_attn, "avg_ms": round(sep_ms, 5),
+                                     "note": "kvq_rotate_quantize_append of the 16 decode tokens, then "
+                                             "kvq_paged_decode_attention"},
         "paged_decode_attention_alone": {
             "bytes": b_attn, "avg_ms": round(dec_avg, 5), "launches": 20 * n_blk,
             "block_median_ms": round(float(np.median(dec_only_ms)), 5),
@@ -697,7 +723,7 @@ def main():
             "GBps": round(gbps(b_attn, dec_avg), 1), "frac_of_peak": round(gbps(b_attn, dec_avg) / PEAK_HBM_GBPS, 4),
             "decode_tokens_per_s": round(shape.batch / (dec_avg * 1e-3), 1)},
     }
-    dominant = "rotate_quantize_append_prefill" if pre_avg >= attn_avg else "paged_decode_attention_alone"
+    dominant = "rotate_quantize_append_prefill" if pre_avg >= dec_avg else "paged_decode_attention_alone"
     dom_bytes, dom_ms = (b_prefill, pre_avg) if dominant.startswith("rotate") else (b_attn, dec_avg)
     achieved = gbps(dom_bytes, dom_ms)
     t_app = stored_traffic(shape.name, "append_kernel")
@@ -717,7 +743,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "storage": f"int{shape.bits} codes + fp32 scale/zero",
         "data": "synthetic (seeded bf16 K/V/Q: N(0,1), 4 outlier channels x10, per-token LogNormal(0,1) norms)",
         "config": {"workload": f"{shape.name}: {shape.batch} seq x {shape.context_lens[0]} tokens prefill-append + "
-                               f"1 decode step (append + attention over {max_len}), {shape.num_q_heads}/"
+                               f"1 fused decode step (append + attention over {max_len}), {shape.num_q_heads}/"
                                f"{shape.num_kv_heads} heads, head_dim 128, page 16, Hadamard block {hb}, "
                                f"INT{shape.bits}",
                    "global_batch": shape.batch, "seq_len": max_len, "parallelism": "single GPU"},
