@@ -19,6 +19,9 @@ It is the plain definition of what the method computes, written out slowly with 
   matrix, scores are softmax(q k / sqrt(D)), and one inverse rotation on the output undoes
   the rotation of V.
 
+* Several queries per sequence (chunked prefill, speculative verification) -- the same attention
+  with a causal limit per query: the paged low-bit attention of the OSCAR abstract applied to the
+  prefill side.
 * Baseline -- attention over an unquantized bf16 paged cache (``PagedCacheBF16``,
   ``append_bf16``, ``decode_bf16``): the BF16 split decode the OScaR abstract (thelatestinai.com
   page) measures its speed-up against, used to put the low-bit path's speed next to it.
@@ -63,7 +66,7 @@ __all__ = [
     "hadamard", "rotation_matrix", "rotate_f32", "token_rms", "quantize_rows",
     "rotate_quantize", "pack_rows", "unpack_rows", "PagedCache", "append",
     "gather_sequence", "attend", "decode", "dequant_page", "bf16_to_f32",
-    "PagedCacheBF16", "append_bf16", "decode_bf16",
+    "PagedCacheBF16", "append_bf16", "decode_bf16", "multi_query_attention",
 ]
 
 
@@ -303,6 +306,40 @@ def decode(cache: PagedCache, q_bits: np.ndarray, block_table: np.ndarray, conte
         qr = q if q_prerotated else r @ q
         o_rot = attend(qr, kh, vh, scale)
         out[b, h] = (r.T @ o_rot).astype(np.float32)
+    return out
+
+
+def multi_query_attention(cache: PagedCache, q_bits: np.ndarray, q_lens: np.ndarray, block_table: np.ndarray,
+                          context_lens: np.ndarray, num_kv_heads: int, hadamard_block: int, softmax_scale: float = 0.0,
+                          q_prerotated: int = 0, rows=None) -> np.ndarray:
+    """Attention of several new tokens per sequence over the paged cache, causal (chunked prefill,
+    speculative verification): sequence b's q_lens[b] queries are its last q_lens[b] tokens, already
+    in the cache, so query j (0-based) sits at position context_lens[b] - q_lens[b] + j and attends
+    to tokens 0 .. that position. q_bits bf16 [B, Q, Hq, d]; returns float32 [B, Q, Hq, d] in the
+    un-rotated basis, zeros for j >= q_lens[b]. ``rows`` optionally restricts the work to (b, j, h)
+    triples (others NaN)."""
+    bsz, qmax, hq, d = q_bits.shape
+    g = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(d)
+    r = rotation_matrix(d, hadamard_block)
+    out = np.full((bsz, qmax, hq, d), np.nan if rows is not None else 0.0, dtype=np.float32)
+    todo = rows if rows is not None else [(b, j, h) for b in range(bsz) for j in range(int(q_lens[b]))
+                                          for h in range(hq)]
+    cached = {}
+    for b, j, h in todo:
+        if j >= int(q_lens[b]):
+            out[b, j, h] = 0.0
+            continue
+        kvh = h // g
+        length = int(context_lens[b])
+        key = (b, kvh)
+        if key not in cached:
+            cached = {key: gather_sequence(cache, block_table[b], length, kvh)}
+        kh, vh = cached[key]
+        n = length - int(q_lens[b]) + j + 1          # causal: the query's own position included
+        q = bf16_to_f32(q_bits[b, j, h]).astype(np.float64)
+        qr = q if q_prerotated else r @ q
+        out[b, j, h] = (r.T @ attend(qr, kh[:n], vh[:n], scale)).astype(np.float32)
     return out
 
 

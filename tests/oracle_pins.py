@@ -456,6 +456,43 @@ def pin_decode_quantization_error_small():
     assert errs[128] < errs[1]
 
 
+def pin_multi_query_attention():
+    """Multi-query attention reduces to decode for one query per sequence, each later query
+    sees exactly one more token (equal to decode over the shorter prefix), queries past q_lens are
+    zero, and the result matches a dense causal softmax (torch SDPA with a causal mask) on the
+    dequantized, rotated-back cache."""
+    import torch
+    shape = _small_shape(hq=4, hkv=2, lens=(40, 19, 7))
+    plan = W.plan_pages(shape, 0)
+    cache, k, v, slots, _ = _filled_cache(shape, plan)
+    lens = np.array(shape.context_lens)
+    rng = np.random.default_rng(31)
+    qmax = 5
+    q = _bits(rng.standard_normal((3, qmax, 4, 128)))
+    q_lens = np.array([5, 1, 3])
+    out = O.multi_query_attention(cache, q, q_lens, plan.block_table, lens, 2, 32)
+    assert np.all(out[1, 1:] == 0) and np.all(out[2, 3:] == 0)
+    # q_len 1 is the decode of that query
+    dec = O.decode(cache, q[:, 0], plan.block_table, lens - q_lens + 1, 2, 32)
+    for b in range(3):
+        assert np.array_equal(out[b, 0], dec[b]), b
+    # query j equals decode over the prefix ending at its own position
+    for j in range(5):
+        d_j = O.decode(cache, q[:, j], plan.block_table, lens - q_lens + j + 1, 2, 32)
+        assert np.array_equal(out[0, j], d_j[0]), j
+    # dense causal attention of the last 5 positions of sequence 0, with the rotation undone
+    r = O.rotation_matrix(128, 32)
+    for h in range(4):
+        kh, vh = O.gather_sequence(cache, plan.block_table[0], 40, h // 2)
+        qq = np.stack([r @ O.bf16_to_f32(q[0, j, h]).astype(np.float64) for j in range(5)])
+        mask = np.arange(40)[None, :] <= (35 + np.arange(5))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qq)[None], torch.from_numpy(kh.astype(np.float64))[None],
+            torch.from_numpy(vh.astype(np.float64))[None], attn_mask=torch.from_numpy(mask)[None])[0].numpy()
+        ref = ref @ r                                   # R^T o, row vectors
+        assert np.allclose(out[0, :, h], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max()), h
+
+
 # ----------------------------------------------------------------------------- bf16 baseline
 
 def pin_bf16_cache_layout():

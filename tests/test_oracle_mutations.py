@@ -194,9 +194,20 @@ def m_bf16_gqa_modulo(mp):
     mp.setattr(O, "decode_bf16", bad)
 
 
+def m_mq_off_by_one(mp):
+    real = O.multi_query_attention
+
+    def bad(cache, q_bits, q_lens, block_table, context_lens, num_kv_heads, hadamard_block, softmax_scale=0.0,
+            q_prerotated=0, rows=None):
+        # each query also sees the token after its own position
+        return real(cache, q_bits, q_lens, block_table, np.asarray(context_lens) + 1, num_kv_heads, hadamard_block,
+                    softmax_scale, q_prerotated, rows)
+    mp.setattr(O, "multi_query_attention", bad)
+
+
 MUTATIONS = [m_hadamard_sign, m_hadamard_row_order, m_rotation_norm, m_round_half_up, m_qmax_off_by_one,
              m_zero_is_max, m_pack_high_first, m_v_interleave_swapped, m_no_softmax_scale,
-             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo]
+             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo, m_mq_off_by_one]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
