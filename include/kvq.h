@@ -164,6 +164,35 @@ kvq_status kvq_paged_decode_attention(
     hipStream_t stream);
 
 /*
+ * Several queries per sequence - chunked prefill, speculative verification: the causal attention
+ * of each sequence's last q_lens[b] tokens, already appended to the cache, over its context (the
+ * paged low-bit attention of the decode, with query tiles of more than one token).
+ *
+ *   q                bf16 [batch][max_q_len][num_q_heads][head_dim]; query j of sequence b sits at
+ *                    position context_lens[b] - q_lens[b] + j and attends to tokens 0 .. that position.
+ *   q_lens           int32 [batch] (device), each in [0, max_q_len]; clamped to context_lens[b].
+ *   out              float32 [batch][max_q_len][num_q_heads][head_dim], un-rotated; rows with
+ *                    j >= q_lens[b] are zero.
+ *   workspace        at least kvq_paged_prefill_workspace_size(...) bytes (same arguments).
+ *   Any number of query heads per KV head. All other arguments as for kvq_paged_decode_attention;
+ *   with max_q_len = 1 and q_lens = 1 it computes the same attention.
+ */
+size_t kvq_paged_prefill_workspace_size(
+    int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t page_size, int32_t pages_per_split);
+
+kvq_status kvq_paged_prefill_attention(
+    const uint16_t* q, int32_t q_prerotated, const int32_t* q_lens, int32_t max_q_len,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream);
+
+/*
  * Fused decode step: append each sequence's new token and attend, in one launch (the fused
  * pipeline of the OSCAR abstract on the thelatestinai.com page; one launch per layer per step).
  * Equivalent to kvq_rotate_quantize_append of k_new[b], v_new[b] at the slot of position

@@ -34,10 +34,10 @@ struct WorkspaceLayout {
   size_t acc_bytes, ml_offset, total;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_q_heads) {
+WorkspaceLayout workspace_layout(int32_t num_splits, int32_t batch, int32_t num_q_heads, int32_t q_len_max = 1) {
   WorkspaceLayout w{0, 0, 0};
   if (num_splits <= 1) return w;
-  const size_t rows = static_cast<size_t>(num_splits) * batch * num_q_heads;
+  const size_t rows = static_cast<size_t>(num_splits) * batch * q_len_max * num_q_heads;
   w.acc_bytes = rows * kvq::kHeadDim * sizeof(float);
   w.ml_offset = round_up(w.acc_bytes);
   w.total = w.ml_offset + round_up(rows * 2 * sizeof(float));
@@ -209,15 +209,19 @@ kvq_status decode_args(
     const int32_t* context_lens, int32_t max_context_len,
     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t hadamard_block, int32_t bits, float softmax_scale,
-    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split) {
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, int32_t q_len_max = 0) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
-      max_pages_per_seq < 0 || pages_per_split < 0)
+      max_pages_per_seq < 0 || pages_per_split < 0 || q_len_max < 0)
     return KVQ_ERR_SHAPE;
   if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
   if (num_q_heads % num_kv_heads) return KVQ_ERR_SHAPE;
   if (q_prerotated != 0 && q_prerotated != 1) return KVQ_ERR_SHAPE;
-  if (num_q_heads / num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
-  if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  // one query per sequence: the heads of a KV head are the columns of one wave (at most 8);
+  // several: columns are (query, head) pairs in tiles of 16, any group size
+  if (q_len_max == 0 && num_q_heads / num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+  const int32_t tiles = q_len_max > 0 ? kvq::mq_column_tiles(q_len_max, num_q_heads / num_kv_heads) : 1;
+  if (num_kv_heads > 65535 || batch > 65535 || static_cast<int64_t>(num_kv_heads) * tiles > 65535)
+    return KVQ_ERR_UNSUPPORTED;
   const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
@@ -226,11 +230,12 @@ kvq_status decode_args(
       !aligned(v_sz, 8) || !aligned(block_table, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_SHAPE;
 
-  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
-  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
+  const kvq::SplitPlan plan = kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads, q_len_max > 0 ? q_len_max : 1);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
 
   a = kvq::DecodeArgs{};
+  a.q_len_max = q_len_max;
   a.q = q;
   a.q_prerotated = q_prerotated;
   a.k_codes = k_codes;
@@ -356,6 +361,45 @@ kvq_status kvq_dequant_page(
   return kvq::launch_dequant(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+
+// ---------------------------------------------------------------------------- several queries
+
+size_t kvq_paged_prefill_workspace_size(int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len, int32_t page_size,
+                                        int32_t pages_per_split) {
+  if (batch <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      head_dim != kvq::kHeadDim || page_size <= 0 || max_context_len < 0 || pages_per_split < 0)
+    return 0;
+  const int32_t tiles = kvq::mq_column_tiles(max_q_len, num_q_heads / num_kv_heads);
+  const kvq::SplitPlan p = kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split);
+  return workspace_layout(p.num_splits, batch, num_q_heads, max_q_len).total;
+}
+
+kvq_status kvq_paged_prefill_attention(
+    const uint16_t* q, int32_t q_prerotated, const int32_t* q_lens, int32_t max_q_len,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+    hipStream_t stream) {
+  if (max_q_len <= 0) return KVQ_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * max_q_len > 0x7FFFFFFF / 128) return KVQ_ERR_UNSUPPORTED;
+  kvq::DecodeArgs a;
+  if (kvq_status s = decode_args(a, q, q_prerotated, k_codes, v_codes, k_sz, v_sz, num_pages, page_size, block_table,
+                                 max_pages_per_seq, context_lens, max_context_len, batch, num_q_heads, num_kv_heads,
+                                 head_dim, hadamard_block, bits, softmax_scale, out, workspace, workspace_bytes,
+                                 pages_per_split, max_q_len))
+    return s;
+  if (batch == 0) return KVQ_OK;
+  if (!q_lens) return KVQ_ERR_NULL;
+  if (!aligned(q_lens, 4)) return KVQ_ERR_SHAPE;
+  a.q_lens = q_lens;
+  a.use_valu = 0;  // the matrix-core kernel only
+  return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
 
 // ---------------------------------------------------------------------------- bf16 baseline
 

@@ -303,16 +303,22 @@ __device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int BITS, bool PS16, int NT>
+// MQ = false: decode, one query per sequence; the 16 columns of the QK output (lane n) are the
+// query heads of one KV head (n < g used). MQ = true: several queries per sequence; a wave takes a
+// tile of 16 columns out of the (query token, head) pairs of one KV head, column c meaning query
+// c / g, head c % g, each with its own causal length.
+template <int BITS, bool PS16, int NT, bool MQ>
 __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
-  __shared__ float qs[8][kHeadDim];
+  constexpr int kQRows = MQ ? 16 : 8;  // query vectors staged per wave
+  __shared__ float qs[kQRows][kHeadDim];
   __shared__ float4 szs[2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
 
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
   const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads) : static_cast<int>(blockIdx.y);
+  const int c0 = MQ ? 16 * static_cast<int>(blockIdx.y / a.num_kv_heads) : 0;  // first column of the tile
   const int b = blockIdx.z;
   const int g = a.num_q_heads / a.num_kv_heads;
   const int ps = PS16 ? 16 : a.page_size;
@@ -322,7 +328,21 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   const int p_begin = split * a.pages_per_split;
   // the last split also takes the pages past num_splits * pages_per_split (see plan_splits)
   const int p_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split);
-  const int64_t q_row0 = (static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g) * kHeadDim;
+  // queries of this sequence (MQ; never more than its tokens) and the tile's valid columns
+  const int qlen = MQ ? min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len) : 1;
+  const int ncols = MQ ? min(16, qlen * g - c0) : g;
+  const int ncols_rows = MQ ? min(16, a.q_len_max * g - c0) : g;  // columns that are rows of out
+  // row (in head vectors) of q / out for local column c
+  auto col_row = [&](int c) -> int64_t {
+    if constexpr (MQ) {
+      const int cc = c0 + c;
+      return (static_cast<int64_t>(b) * a.q_len_max + cc / g) * a.num_q_heads + static_cast<int64_t>(kvh) * g + cc % g;
+    } else {
+      return static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g + c;
+    }
+  };
+  // causal length of this lane's column (MQ), else the sequence length
+  const int len_col = MQ ? ((n < ncols) ? len - qlen + (c0 + n) / g + 1 : 0) : len;
 
   if (a.fused && len > 0) {
     // this split owns the last page: write the new token first
@@ -334,10 +354,10 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     }
   }
 
-  if (p_begin >= p_end) {
-    if (a.num_splits == 1) {  // empty sequence: zero output
-      for (int h = G; h < g; h += 4) {
-        float4* o = reinterpret_cast<float4*>(a.out + q_row0 + h * kHeadDim + n * 8);
+  if (p_begin >= p_end || ncols <= 0) {
+    if (a.num_splits == 1) {  // empty sequence (or no valid query in the tile): zero output
+      for (int c = G; c < ncols_rows; c += 4) {
+        float4* o = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + n * 8);
         o[0] = make_float4(0.f, 0.f, 0.f, 0.f);
         o[1] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -348,7 +368,8 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // ---- walk the split's tiles, NT per step, the next two steps loading meanwhile
   const int tile_begin = p_begin * tiles_per_page;
   const int tile_end = min(p_end * tiles_per_page, (len + 15) / 16);
-  const int full_end = min(tile_end, len / 16);  // tiles before this one are entirely valid
+  // tiles before full_end are valid for every column (MQ: the tile's first query is the most limited)
+  const int full_end = min(tile_end, (MQ ? len - qlen + c0 / g + 1 : len) / 16);
   const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages_per_seq;
 
   v4f acc[8];
@@ -383,11 +404,12 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 
   // The query rows (row group G: heads G and G + 4) and then the first four tiles start loading
   // before the query is prepared; every lane loads (heads past the group re-read the last one).
-  uint4 qw[2];
+  constexpr int kQPerGroup = kQRows / 4;
+  uint4 qw[kQPerGroup];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int h = min(4 * r + G, g - 1);
-    qw[r] = *reinterpret_cast<const uint4*>(a.q + q_row0 + h * kHeadDim + n * 8);
+  for (int r = 0; r < kQPerGroup; ++r) {
+    const int c = min(4 * r + G, ncols - 1);
+    qw[r] = *reinterpret_cast<const uint4*>(a.q + col_row(c) * kHeadDim + n * 8);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads (in-order vmcnt)
   TileCodes x0[NT], x1[NT], x2[NT];
@@ -398,9 +420,9 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // ---- query: rotate (R q), scale by softmax_scale * log2(e), stage in LDS in natural order
   const LaneFwht lf = lane_fwht(a.rot, n);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int h = 4 * r + G;
-    if (4 * r >= g) break;
+  for (int r = 0; r < kQPerGroup; ++r) {
+    const int c = 4 * r + G;
+    if (4 * r >= ncols) break;
     float x[8];
     bf16x8_to_f32(qw[r], x);
     int pos = n;
@@ -408,9 +430,9 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
       fwht_row16_planned(x, a.rot, lf);
       pos = lf.pos;
     }
-    if (h < g) {
+    if (c < ncols) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) qs[h][8 * pos + k] = x[k] * a.qk_scale_log2;
+      for (int k = 0; k < 8; ++k) qs[c][8 * pos + k] = x[k] * a.qk_scale_log2;
     }
   }
   wave_lds_sync();
@@ -425,7 +447,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = (n < g) ? qs[n][qk_channel<BITS>(G, j, r, k)] : 0.f;
+      for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = (n < ncols) ? qs[n][qk_channel<BITS>(G, j, r, k)] : 0.f;
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qv[i]));
@@ -511,7 +533,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
       for (int i = 0; i < 4; ++i) {
         float t = __builtin_fmaf(kd[i], static_cast<float>(sc[u][i]), kz[i] * sum_q);
         if constexpr (!full) {
-          const bool ok = pg[u] >= 0 && (tile + u) * 16 + 4 * G + i < len;
+          const bool ok = pg[u] >= 0 && (tile + u) * 16 + 4 * G + i < len_col;
           t = ok ? t : kNegInf;
         }
         sr[4 * u + i] = t;
@@ -652,14 +674,14 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   if (a.num_splits == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * G + i;
+      const int c = 4 * G + i;
       float o[8];
       const float inv_l = (lrow[i] > 0.f) ? 1.0f / lrow[i] : 0.f;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] = (acc[m][i] + zrow[i]) * inv_l;
+      for (int m = 0; m < 8; ++m) o[m] = (c < ncols) ? (acc[m][i] + zrow[i]) * inv_l : 0.f;
       fwht_row16_planned(o, a.rot, lf);  // R^T = R: back to the original basis
-      if (h < g) {
-        float4* dst = reinterpret_cast<float4*>(a.out + q_row0 + h * kHeadDim + 8 * lf.pos);
+      if (c < ncols_rows) {
+        float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf.pos);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
         dst[1] = make_float4(o[4], o[5], o[6], o[7]);
       }
@@ -669,13 +691,12 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 
   // Split: publish this split's partial (un-normalised accumulator with its zero term, running
   // maximum and sum) for the merge kernel.
-  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
-  const int64_t head0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(kvh) * g;
+  const int64_t pairs = static_cast<int64_t>(a.batch) * (MQ ? a.q_len_max : 1) * a.num_q_heads;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * G + i;
-    if (h < g) {
-      const int64_t row = split * pairs + head0 + h;
+    const int c = 4 * G + i;
+    if (c < ncols) {
+      const int64_t row = split * pairs + col_row(c);
       float4* dst = reinterpret_cast<float4*>(a.ws_acc + row * kHeadDim + 8 * n);
       dst[0] = make_float4(acc[0][i] + zrow[i], acc[1][i] + zrow[i], acc[2][i] + zrow[i], acc[3][i] + zrow[i]);
       dst[1] = make_float4(acc[4][i] + zrow[i], acc[5][i] + zrow[i], acc[6][i] + zrow[i], acc[7][i] + zrow[i]);
@@ -705,13 +726,18 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
-  const int64_t pair = blockIdx.x;  // b * num_q_heads + h
-  const int b = static_cast<int>(pair / a.num_q_heads);
+  const int64_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
+  const int q_len_max = a.q_lens ? a.q_len_max : 1;
+  const int b = static_cast<int>(pair / (static_cast<int64_t>(q_len_max) * a.num_q_heads));
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + a.page_size - 1) / a.page_size;
-  const int nu = min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
+  int nu = min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
+  if (a.q_lens) {  // a query row past the sequence's queries has no partials: zero output
+    const int j = static_cast<int>((pair / a.num_q_heads) % q_len_max);
+    if (j >= min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len)) nu = 0;
+  }
   const LaneFwht lf = lane_fwht(a.rot, n);
-  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int64_t pairs = static_cast<int64_t>(a.batch) * q_len_max * a.num_q_heads;
   const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
   float mo = kNegInf, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < nu; s0 += 32) {
@@ -735,7 +761,9 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
     for (int m = 0; m < 8; ++m) o[m] *= r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float f = (s0 + G + 4 * j < nu) ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
+      // a split with no token for this row (several queries: past a query's causal limit) has
+      // maximum -inf and weighs nothing (even when every split so far is such a split)
+      const float f = (s0 + G + 4 * j < nu && ml[j].x != kNegInf) ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
       lsum = __builtin_fmaf(ml[j].y, f, lsum);
       o[0] = __builtin_fmaf(xa[j].x, f, o[0]); o[1] = __builtin_fmaf(xa[j].y, f, o[1]);
       o[2] = __builtin_fmaf(xa[j].z, f, o[2]); o[3] = __builtin_fmaf(xa[j].w, f, o[3]);
@@ -757,27 +785,36 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads),
-                  static_cast<unsigned>(a.batch));
+template <bool MQ>
+hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const bool ps16 = a.page_size == 16;
   constexpr int kNT = KVQ_DECODE_STEP_TILES;
   if (a.bits == 4) {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, kNT>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, kNT>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, kNT, MQ>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, kNT, MQ>), grid, dim3(64), 0, stream, a);
   } else {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, kNT>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, kNT>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, kNT, MQ>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, kNT, MQ>), grid, dim3(64), 0, stream, a);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Column tiles of 16 (query, head) pairs per KV head for several queries per sequence.
+int32_t mq_column_tiles(int32_t q_len_max, int32_t group) { return (q_len_max * group + 15) / 16; }
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned tiles = a.q_lens ? static_cast<unsigned>(mq_column_tiles(a.q_len_max, a.num_q_heads / a.num_kv_heads)) : 1u;
+  const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
+                  static_cast<unsigned>(a.batch));
+  hipError_t e = a.q_lens ? launch_kernel<true>(a, grid, stream) : launch_kernel<false>(a, grid, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   return launch_decode_merge(a, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int64_t pairs = static_cast<int64_t>(a.batch) * (a.q_lens ? a.q_len_max : 1) * a.num_q_heads;
   hipLaunchKernelGGL(decode_merge_splits_kernel, dim3(static_cast<unsigned>(pairs)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

@@ -72,6 +72,11 @@ struct DecodeArgs {
   int32_t pages_per_split;
   float* ws_acc;                  // [num_splits][batch][num_q_heads][128]
   float* ws_ml;                   // [num_splits][batch][num_q_heads][2]  (max, sum) in log2 units
+  // Several queries per sequence (chunked prefill, speculative verification): q and out are
+  // [batch][q_len_max][num_q_heads][128]; sequence b's q_lens[b] queries are its last q_lens[b]
+  // tokens, causal. nullptr for the decode (one query per sequence).
+  const int32_t* q_lens;
+  int32_t q_len_max;
   // Fused decode step: before attending, the wave that owns a sequence's last page rotates,
   // quantizes and writes that sequence's new token (position context_lens[b] - 1) for its KV head.
   int32_t fused;
@@ -139,6 +144,8 @@ hipError_t launch_decode_bf16(const DecodeBf16Args& a, hipStream_t stream);
 // given by a.rot (the identity plan for block size 1); reads a.context_lens, a.max_context_len,
 // a.page_size, a.pages_per_split, a.num_splits, a.batch, a.num_q_heads.
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+// Column tiles (16 (query, head) pairs each) per KV head when a sequence has q_len_max queries.
+int32_t mq_column_tiles(int32_t q_len_max, int32_t group);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);

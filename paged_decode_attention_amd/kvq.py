@@ -19,7 +19,8 @@ KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
            "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page",
-           "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step")
+           "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step",
+           "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention")
 
 
 class KVQError(RuntimeError):
@@ -56,6 +57,12 @@ def lib() -> ctypes.CDLL:
         _p, _p, _sz, _i32, _p]
     L.kvq_dequant_page.restype = _i32
     L.kvq_dequant_page.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
+    L.kvq_paged_prefill_workspace_size.restype = _sz
+    L.kvq_paged_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    L.kvq_paged_prefill_attention.restype = _i32
+    L.kvq_paged_prefill_attention.argtypes = [
+        _p, _i32, _p, _i32, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        _p, _p, _sz, _i32, _p]
     L.kvq_decode_step.restype = _i32
     L.kvq_decode_step.argtypes = [
         _p, _i32, _p, _p, _i64, _i64, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -214,6 +221,50 @@ def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: to
         hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32), ws_ptr, ws_bytes,
         pages_per_split, _stream(stream))
     _check(st, "kvq_paged_decode_attention")
+    return out
+
+
+def prefill_workspace_size(batch: int, max_q_len: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
+                           page_size: int, pages_per_split: int = 0) -> int:
+    return int(lib().kvq_paged_prefill_workspace_size(batch, max_q_len, num_q_heads, num_kv_heads, HEAD_DIM,
+                                                       max_context_len, page_size, pages_per_split))
+
+
+def paged_prefill_attention(q: torch.Tensor, q_lens: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
+                            context_lens: torch.Tensor, max_context_len: int, hadamard_block: int,
+                            softmax_scale: float = 0.0, q_prerotated: int = 0, out: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, pages_per_split: int = 0,
+                            stream=None) -> torch.Tensor:
+    """kvq_paged_prefill_attention: q bf16 [B, Q, Hq, 128], q_lens int32 [B] -> float32 [B, Q, Hq, 128]."""
+    cache._check_layout()
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Q, Hq, 128] tensor")
+    bsz, qmax, hq, _ = q.shape
+    if q_lens.shape != (bsz,) or not q_lens.is_contiguous():
+        raise ValueError("q_lens must be a contiguous [B] int32 tensor")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] int32 tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+    if out is None:
+        out = torch.empty((bsz, qmax, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (bsz, qmax, hq, HEAD_DIM) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Q, Hq, 128] float32 tensor")
+    need = prefill_workspace_size(bsz, qmax, hq, cache.num_kv_heads, max_context_len, cache.page_size,
+                                  pages_per_split)
+    if workspace is None and need > 0:
+        workspace = decode_workspace(need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().kvq_paged_prefill_attention(
+        _dev(q, "q", torch.bfloat16), q_prerotated, _dev(q_lens, "q_lens", torch.int32), qmax,
+        _dev(cache.k_codes, "k_codes", torch.uint8), _dev(cache.v_codes, "v_codes", torch.uint8),
+        _dev(cache.k_sz, "k_sz", torch.float32), _dev(cache.v_sz, "v_sz", torch.float32),
+        cache.num_pages, cache.page_size, _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, bsz, hq, cache.num_kv_heads, HEAD_DIM,
+        hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32), ws_ptr, ws_bytes,
+        pages_per_split, _stream(stream))
+    _check(st, "kvq_paged_prefill_attention")
     return out
 
 

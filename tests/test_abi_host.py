@@ -179,3 +179,22 @@ def test_decode_step_validation():
     assert step(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
     assert step(ts=2) == kvq.KVQ_ERR_SHAPE
     assert step(ks=1000) == kvq.KVQ_ERR_SHAPE
+
+
+def test_prefill_validation_and_workspace():
+    L = kvq.lib()
+
+    def pre(**kw):
+        return L.kvq_paged_prefill_attention(
+            NULL, 0, NULL, kw.get("ql", 4), NULL, NULL, NULL, NULL, 10, 16, NULL, 4, NULL, 64, kw.get("b", 2),
+            kw.get("hq", 32), 8, 128, 128, kw.get("bits", 4), 0.0, NULL, NULL, 0, 0, NULL)
+    assert pre() == kvq.KVQ_ERR_NULL
+    assert pre(b=0) == kvq.KVQ_OK
+    assert pre(ql=0) == kvq.KVQ_ERR_SHAPE
+    assert pre(hq=30) == kvq.KVQ_ERR_SHAPE
+    assert pre(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
+    assert pre(hq=8 * 24) == kvq.KVQ_ERR_NULL      # 24 heads per KV head are fine with several queries
+    # workspace: one split when the (sequence, KV head, column tile) items fill the GPU
+    assert L.kvq_paged_prefill_workspace_size(64, 16, 32, 8, 128, 4096, 16, 0) == 0
+    w = L.kvq_paged_prefill_workspace_size(1, 4, 32, 8, 128, 4096, 16, 0)
+    assert w >= 2 * 4 * 32 * 130 * 4
