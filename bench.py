@@ -484,6 +484,50 @@ def suite_oscar(dev, stream, cpu):
     return [row]
 
 
+def suite_multi_query(dev, stream, cpu):
+    """Several queries per sequence over the low-bit cache: speculative verification (4 draft
+    tokens per sequence, Llama-3-8B shape) and a 512-token chunk of chunked prefill (OScaR INT2
+    shape: the chunk's attention over its sequence so far)."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    rows = []
+    for name, qlen in (("llama3_8b", 4), ("oscar_int2", 512)):
+        shape = W.config(name)
+        plan = W.plan_pages(shape, extra_tokens=1)
+        caches = _filled_caches(shape, plan, 4, dev, stream)
+        lens = np.asarray(shape.context_lens, dtype=np.int32)  # the last qlen tokens are the queries
+        g = torch.Generator(device=dev)
+        g.manual_seed(shape.seed + qlen)
+        q = torch.randn((shape.batch, qlen, shape.num_q_heads, 128), generator=g, device=dev).to(torch.bfloat16)
+        q_lens = torch.full((shape.batch,), qlen, dtype=torch.int32, device=dev)
+        bt = torch.from_numpy(plan.block_table).to(dev)
+        lens_d = torch.from_numpy(lens).to(dev)
+        max_len = int(lens.max())
+        ws = kvq.decode_workspace(kvq.prefill_workspace_size(shape.batch, qlen, shape.num_q_heads, shape.num_kv_heads,
+                                                             max_len, shape.page_size), dev)
+        out = torch.empty((shape.batch, qlen, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+        def run(i):
+            kvq.paged_prefill_attention(q, q_lens, caches[i % 4], bt, lens_d, max_len, shape.hadamard_block,
+                                        out=out, workspace=ws, stream=stream)
+        for i in range(3):
+            run(i)
+        ms = _timed(run, 20, stream)
+        nbytes = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+        # multiply-adds of QK and PV over the causal window of every query
+        causal = float(np.sum([qlen * (int(n) - qlen) + qlen * (qlen + 1) / 2 for n in lens]))
+        flops = 4.0 * 128 * shape.num_q_heads * causal
+        rows.append(_line(workload=f"{name} shape, {qlen} queries per sequence "
+                                   f"({'speculative verification' if qlen < 16 else 'chunked-prefill chunk'})",
+                          batch=shape.batch, queries_per_seq=qlen, attention_ms=round(ms, 5),
+                          cache_read_GBps=round(nbytes / ms / 1e6, 1), attention_TFLOPs=round(flops / ms / 1e9, 2),
+                          query_tokens_per_s=round(shape.batch * qlen / (ms * 1e-3), 1)))
+        del caches
+        torch_empty_cache()
+    return rows
+
+
 def suite_tiny(dev, stream, cpu):
     import torch
     from paged_decode_attention_amd import kvq
@@ -534,7 +578,7 @@ def run_suite(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     rows = []
-    for fn in (suite_tiny, suite_sweep, suite_llama2_70b, suite_oscar):
+    for fn in (suite_tiny, suite_sweep, suite_llama2_70b, suite_oscar, suite_multi_query):
         new = fn(dev, stream, args.suite_cpu)
         for r in new:
             print(json.dumps(r), flush=True)
