@@ -700,19 +700,38 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: K steps with one event pair around them (no markers between the launches)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+
+    # the same K steps again with an event between every launch: per-launch times inside the step (each event
+    # adds a marker packet, a few us per launch)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
     prefill_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dstep_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    # the prefill append back to back in blocks of 5 launches between events, rotating over the input and
+    # cache copies: its launch duration without marker overhead (the roofline's time)
+    n_pblk = max(2, args.steps // 5)
+    pblk_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_pblk)]
+    for j in range(n_pblk):
+        pblk_ev[j][0].record(stream)
+        for i in range(5):
+            prefill(args.warmup + 5 * j + i)
+        pblk_ev[j][1].record(stream)
+    torch.cuda.synchronize()
+    prefill_blk_ms = np.array([e[0].elapsed_time(e[1]) / 5 for e in pblk_ev])
 
     # the same decode step as two launches (append, then attention), for comparison
     for i in range(5):
@@ -745,9 +764,11 @@ def main():
     def gbps(nbytes, ms):
         return nbytes / (ms * 1e-3) / 1e9
 
-    pre_avg, dstep_avg, dec_avg = float(prefill_ms.mean()), float(dstep_ms.mean()), float(dec_only_ms.mean())
+    pre_avg, dstep_avg, dec_avg = float(prefill_blk_ms.mean()), float(dstep_ms.mean()), float(dec_only_ms.mean())
     kernels = {
         "rotate_quantize_append_prefill": {"bytes": b_prefill, "avg_ms": round(pre_avg, 5),
+                                           "launches": 5 * n_pblk,
+                                           "in_step_event_ms": round(float(prefill_ms.mean()), 5),
                                            "GBps": round(gbps(b_prefill, pre_avg), 1),
                                            "frac_of_peak": round(gbps(b_prefill, pre_avg) / PEAK_HBM_GBPS, 4),
                                            "tokens_per_s": round(len(seq) / (pre_avg * 1e-3), 1)},

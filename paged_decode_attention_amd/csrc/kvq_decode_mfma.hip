@@ -30,14 +30,14 @@
 #include "kvq_device.h"
 #include "kvq_launch.h"
 
-#ifndef KVQ_DECODE_STEP_TILES
-#define KVQ_DECODE_STEP_TILES 2   // 16-token tiles per step (2 or 4)
-#endif
 #ifndef KVQ_DECODE_MIN_WAVES
 #define KVQ_DECODE_MIN_WAVES 2    // waves per SIMD the register allocation must allow
 #endif
-#ifndef KVQ_DECODE_PREFETCH_STEPS
-#define KVQ_DECODE_PREFETCH_STEPS 2  // steps of tiles loading while one is processed (2 or 3)
+#ifndef KVQ_DECODE_PACK
+// Most tiles whose scores share one QK output (1, 2 or 4). Two is the fastest measured on every
+// workload shape: four needs four-tile steps, and with only two step buffers in registers the
+// loads are covered by one step of work instead of two.
+#define KVQ_DECODE_PACK 2
 #endif
 
 namespace kvq {
@@ -189,6 +189,10 @@ struct LaneOffsets {
   const float* sz;     // this lane's scale/zero array (K for lanes 0..31, V for 32..63) + lane offset
 };
 
+// The code and scale/zero loads are non-temporal (cache policy nt): every byte of the cache is
+// read once per call, so it should not displace the page table, queries and partials in L2.
+constexpr int kCodeAux = 2;
+
 // Loads one tile whose first token row (in the [page][head][token] row numbering shared by the
 // code and scale/zero arrays) is row0.
 template <int BITS>
@@ -199,15 +203,15 @@ __device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t row0
   const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + off, 16 << kRowShift);
   TileCodes t;
   if constexpr (BITS == 4) {
-    t.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k, 0, 0));
-    t.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lo.v, 0, 0));
+    t.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k, 0, kCodeAux));
+    t.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, lo.v, 0, kCodeAux));
   } else {
-    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(kr, lo.k, 0, 0));
-    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, lo.v, 0, 0));
+    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(kr, lo.k, 0, kCodeAux));
+    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, lo.v, 0, kCodeAux));
     t.k = make_uint4(k2.x, k2.y, 0, 0);
     t.v = make_uint4(v2.x, v2.y, 0, 0);
   }
-  t.sz = lo.sz[row0 * 2];
+  t.sz = __builtin_nontemporal_load(lo.sz + row0 * 2);
   return t;
 }
 
@@ -303,19 +307,40 @@ __device__ __forceinline__ void append_new_token(const DecodeArgs& a, int b, int
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// MQ = false: decode, one query per sequence; the 16 columns of the QK output (lane n) are the
-// query heads of one KV head (n < g used). MQ = true: several queries per sequence; a wave takes a
-// tile of 16 columns out of the (query token, head) pairs of one KV head, column c meaning query
-// c / g, head c % g, each with its own causal length.
-template <int BITS, bool PS16, int NT, bool MQ>
+// Rotation inside each 16-lane row (DPP row_ror): every lane takes the value of the lane R places
+// along its row, wrapping around.
+template <int R>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + R, 0xF, 0xF, false));
+}
+
+// MQ = false: decode, one query per sequence. The 16 columns of the QK output are F tile slots of
+// W = 16 / F columns: column n holds query head n % W (used while below g) against the tokens of
+// tile n / W of the group, so one output carries the scores of F tiles and every lane's softmax
+// work is useful (F = 4 for g <= 4, 2 for g <= 8). The PV product then keeps one accumulator row
+// per (tile slot, head); the slots are summed once, at the end.
+// MQ = true: several queries per sequence (F = 1); a wave takes a tile of 16 columns out of the
+// (query token, head) pairs of one KV head, column c meaning query c / g, head c % g, each with
+// its own causal length.
+// NT tiles per step: 4 with F = 4 (two step buffers), else 2 (three step buffers).
+template <int BITS, bool PS16, int NT, bool MQ, int F>
 __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
+  static_assert(F == 1 || F == 2 || F == 4, "pack factor");
+  static_assert(NT % 2 == 0 && NT % F == 0, "a step holds whole PV chunks and whole packed groups");
+  static_assert(!MQ || F == 1, "several queries fill the 16 columns themselves");
+  constexpr int W = 16 / F;   // columns per tile slot
+  constexpr int KG = NT / F;  // packed score groups per step
+  constexpr int P = 4 * KG;   // scores per lane per step
   constexpr int kQRows = MQ ? 16 : 8;  // query vectors staged per wave
   __shared__ float qs[kQRows][kHeadDim];
   __shared__ float4 szs[2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
+  __shared__ float4 red[F > 1 ? 16 : 1][kHeadDim / 4];  // accumulator rows, for the sum over tile slots
 
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
+  const int u_l = n / W;  // tile slot of this lane's column
+  const int h_l = n % W;  // query column of this lane
   const int split = blockIdx.x;
   const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads) : static_cast<int>(blockIdx.y);
   const int c0 = MQ ? 16 * static_cast<int>(blockIdx.y / a.num_kv_heads) : 0;  // first column of the tile
@@ -365,7 +390,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     return;
   }
 
-  // ---- walk the split's tiles, NT per step, the next two steps loading meanwhile
+  // ---- walk the split's tiles, NT per step, the next NT to 2 NT tiles loading meanwhile
   const int tile_begin = p_begin * tiles_per_page;
   const int tile_end = min(p_end * tiles_per_page, (len + 15) / 16);
   // tiles before full_end are valid for every column (MQ: the tile's first query is the most limited)
@@ -375,14 +400,14 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   v4f acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;   // running maximum of head n (log2 units), equal in the 4 lanes of head n
-  float l_part = 0.f;      // this lane's share of sum p (head n)
-  float z_part = 0.f;      // this lane's share of sum p (z - B delta) (head n)
+  float m_run = kNegInf;   // running maximum of head h_l (log2 units), equal in every lane of the head
+  float l_part = 0.f;      // this lane's share of sum p (head h_l)
+  float z_part = 0.f;      // this lane's share of sum p (z - B delta) (head h_l)
   const float lazy = kLazyRescale;
 
-  // Page of a tile (scalar load). Tiles past the split's end read the last tile again - an L2 hit,
-  // masked out through pg = -1 - so that every fetch issues the same loads and the wait for a
-  // buffer never has to drain the loads of the next one.
+  // Page of a tile (scalar load). Tiles past the split's end read the last tile again (masked out
+  // through pg = -1), so that every fetch issues the same loads and the wait for a buffer never
+  // has to drain the loads of the next one.
   LaneOffsets lo;
   lo.k = (BITS == 4) ? (n * (kHeadDim / 2) + 16 * G) : (n * (kHeadDim / 4) + 8 * G);
   lo.v = (BITS == 4) ? (G * 4 * (kHeadDim / 2) + 16 * n) : (G * 4 * (kHeadDim / 4) + 8 * n);
@@ -402,8 +427,8 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     }
   };
 
-  // The query rows (row group G: heads G and G + 4) and then the first four tiles start loading
-  // before the query is prepared; every lane loads (heads past the group re-read the last one).
+  // The query rows (row group G: heads G and G + 4) and then the first two steps' tiles start
+  // loading before the query is prepared; every lane loads (heads past the group re-read the last one).
   constexpr int kQPerGroup = kQRows / 4;
   uint4 qw[kQPerGroup];
 #pragma unroll
@@ -412,8 +437,8 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     qw[r] = *reinterpret_cast<const uint4*>(a.q + col_row(c) * kHeadDim + n * 8);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep the query loads ahead of the tile loads (in-order vmcnt)
-  TileCodes x0[NT], x1[NT], x2[NT];
-  int64_t pg0[NT], pg1[NT], pg2[NT];
+  TileCodes x0[NT], x1[NT];
+  int64_t pg0[NT], pg1[NT];
   fetch(tile_begin, x0, pg0);
   fetch(tile_begin + NT, x1, pg1);
 
@@ -440,14 +465,14 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // ---- query as 21-bit fixed point x = rint(q' 2^E), |x| <= 2^20, in three int8 limbs: with the
   // offset x + 0x808080 (in [0x708080, 0x908080]) its three bytes b_i are x's base-256 digits
   // shifted by 128, so limb l_i = b_i - 128 is byte b_i with the top bit flipped, and
-  // x = (l2 * 256 + l1) * 256 + l0.
+  // x = (l2 * 256 + l1) * 256 + l0. Column n takes head h_l: the F tile slots share the query.
   float qv[32];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = (n < ncols) ? qs[n][qk_channel<BITS>(G, j, r, k)] : 0.f;
+      for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = (h_l < ncols) ? qs[h_l][qk_channel<BITS>(G, j, r, k)] : 0.f;
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qv[i]));
@@ -495,56 +520,76 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
                        const TileCodes (&next)[NT], int buf) {
     constexpr bool full = decltype(full_tag)::value;
 
-    // QK^T for the step's tiles: one exact int32 dot product per query limb (three independent
+    // QK^T, two tiles at a time: one exact int32 dot product per query limb (six independent
     // MFMA chains of depth two), then x = ((s2 * 256) + s1) * 256 + s0 - Horner's rule on the
-    // finished products, every partial sum below 2^31.
-    v4i sc[NT];
-    {
-      v4i s0[NT], s1[NT], s2[NT];
+    // finished products, every partial sum below 2^31. Tile t's scores then go to packed group
+    // t / F, in the columns of slot t % F.
+    v4i sc[KG];
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const v4i k0 = k_operand<BITS>(c[u].k, 0);
+    for (int t0 = 0; t0 < NT; t0 += 2) {
+      v4i s0[2], s1[2], s2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v4i k0 = k_operand<BITS>(c[t0 + u].k, 0);
         s0[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L0[0], v4i{0, 0, 0, 0}, 0, 0, 0);
         s1[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L1[0], v4i{0, 0, 0, 0}, 0, 0, 0);
         s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k0, L2[0], v4i{0, 0, 0, 0}, 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const v4i k1 = k_operand<BITS>(c[u].k, 1);
+      for (int u = 0; u < 2; ++u) {
+        const v4i k1 = k_operand<BITS>(c[t0 + u].k, 1);
         s0[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L0[1], s0[u], 0, 0, 0);
         s1[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L1[1], s1[u], 0, 0, 0);
         s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L2[1], s2[u], 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < NT; ++u) sc[u] = (((s2[u] << 8) + s1[u]) << 8) + s0[u];
+      for (int u = 0; u < 2; ++u) {
+        const int t = t0 + u;
+        const v4i s = (((s2[u] << 8) + s1[u]) << 8) + s0[u];
+        if (F == 1 || t % F == 0) {
+          sc[t / F] = s;
+        } else {
+          const bool mine = u_l == t % F;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[t / F][i] = mine ? s[i] : sc[t / F][i];
+        }
+      }
     }
 
-    // raw scores t = delta (q~.c) + z sum(q~), in units of 2^E * log2; tokens 4G+i of tile u
-    float sr[4 * NT], vd[4 * NT], vzz[4 * NT];
+    // raw scores t = delta (q~.c) + z sum(q~), in units of 2^E * log2; value 4k + i is token
+    // 4G + i of tile k F + u_l
+    float sr[P], vd[P], vzz[P];
 #pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const float4 k01 = szs[buf][u][2 * G], k23 = szs[buf][u][2 * G + 1];
-      const float4 v01 = szs[buf][u][8 + 2 * G], v23 = szs[buf][u][8 + 2 * G + 1];
+    for (int k = 0; k < KG; ++k) {
+      const float4* zb = szs[buf][k * F + (F > 1 ? u_l : 0)];
+      const float4 k01 = zb[2 * G], k23 = zb[2 * G + 1];
+      const float4 v01 = zb[8 + 2 * G], v23 = zb[8 + 2 * G + 1];
       const float kd[4] = {k01.x, k01.z, k23.x, k23.z};
       const float kz[4] = {k01.y, k01.w, k23.y, k23.w};
       const float vdd[4] = {v01.x, v01.z, v23.x, v23.z};
       const float vz[4] = {v01.y, v01.w, v23.y, v23.w};
+      int64_t pgl = pg[k * F];
+#pragma unroll
+      for (int u = 1; u < F; ++u) pgl = (u_l == u) ? pg[k * F + u] : pgl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float t = __builtin_fmaf(kd[i], static_cast<float>(sc[u][i]), kz[i] * sum_q);
+        float t = __builtin_fmaf(kd[i], static_cast<float>(sc[k][i]), kz[i] * sum_q);
         if constexpr (!full) {
-          const bool ok = pg[u] >= 0 && (tile + u) * 16 + 4 * G + i < len_col;
+          const bool ok = pgl >= 0 && (tile + k * F + u_l) * 16 + 4 * G + i < len_col;
           t = ok ? t : kNegInf;
         }
-        sr[4 * u + i] = t;
-        vd[4 * u + i] = vdd[i];
-        vzz[4 * u + i] = __builtin_fmaf(-VBias<BITS>::value, vdd[i], vz[i]);
+        sr[4 * k + i] = t;
+        vd[4 * k + i] = vdd[i];
+        vzz[4 * k + i] = __builtin_fmaf(-VBias<BITS>::value, vdd[i], vz[i]);
       }
     }
+    // step maximum of each head: over the lane's values, the four row groups and the F slots
     float mt = sr[0];
 #pragma unroll
-    for (int i = 1; i < 4 * NT; ++i) mt = fmaxf(mt, sr[i]);
+    for (int i = 1; i < P; ++i) mt = fmaxf(mt, sr[i]);
     mt = max_over_rows(mt);
+    if constexpr (F >= 2) mt = fmaxf(mt, row_ror<8>(mt));
+    if constexpr (F == 4) mt = fmaxf(mt, row_ror<4>(mt));
     mt *= inv_scale;  // log2 units
     if (__any(mt > m_run + lazy)) {
       const float m_new = (mt > m_run + lazy) ? mt : m_run;
@@ -552,18 +597,19 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
       m_run = m_new;
       l_part *= alpha;
       z_part *= alpha;
-      // accumulator rows are heads 4G+i; their factors live in lane 4G+i (head n = 4G+i)
+      // accumulator row 4G + i is (slot, head (4G + i) % W); that head's factor lives in lane
+      // (4G + i) % W
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * G + i, 64);
+        const float ai = __shfl(alpha, (4 * G + i) & (W - 1), 64);
 #pragma unroll
         for (int m = 0; m < 8; ++m) acc[m][i] *= ai;
       }
     }
     const float m_ref = (m_run == kNegInf) ? 0.f : m_run;  // only a step with no valid token leaves -inf
-    float w[4 * NT];
+    float w[P];
 #pragma unroll
-    for (int i = 0; i < 4 * NT; ++i) {
+    for (int i = 0; i < P; ++i) {
       // p = 2^(t 2^-E - m); invalid tokens have t = -inf and so p = 0
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(inv_scale, sr[i], -m_ref));
       l_part += p;
@@ -575,25 +621,38 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
         w[i] = (sr[i] == kNegInf) ? 0.f : p * vd[i];
       }
     }
+    // PV over chunks of two tiles (32 tokens). A row r = QK column r; with F > 1 a row carries
+    // only the tokens of its own slot's tile, zero for the chunk's other tile.
 #pragma unroll
-    for (int hpair = 0; hpair < NT / 2; ++hpair) {
-      const int u0 = 2 * hpair, u1 = u0 + 1;
-      uint32_t h01a, h23a, l01a, l23a, h01b, h23b, l01b, l23b;
-      split_bf16({w[4 * u0], w[4 * u0 + 1], w[4 * u0 + 2], w[4 * u0 + 3]}, h01a, h23a, l01a, l23a);
-      split_bf16({w[4 * u1], w[4 * u1 + 1], w[4 * u1 + 2], w[4 * u1 + 3]}, h01b, h23b, l01b, l23b);
-      const v8bf p_hi = as_bf(v4u{h01a, h23a, h01b, h23b});
-      const v8bf p_lo = as_bf(v4u{l01a, l23a, l01b, l23b});
+    for (int ch = 0; ch < NT / 2; ++ch) {
+      const int t0 = 2 * ch, t1 = t0 + 1;
+      v8bf p_hi, p_lo;
+      if constexpr (F == 1) {
+        uint32_t h01a, h23a, l01a, l23a, h01b, h23b, l01b, l23b;
+        split_bf16({w[4 * t0], w[4 * t0 + 1], w[4 * t0 + 2], w[4 * t0 + 3]}, h01a, h23a, l01a, l23a);
+        split_bf16({w[4 * t1], w[4 * t1 + 1], w[4 * t1 + 2], w[4 * t1 + 3]}, h01b, h23b, l01b, l23b);
+        p_hi = as_bf(v4u{h01a, h23a, h01b, h23b});
+        p_lo = as_bf(v4u{l01a, l23a, l01b, l23b});
+      } else {
+        const int k = t0 / F;
+        uint32_t h01, h23, l01, l23;
+        split_bf16({w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]}, h01, h23, l01, l23);
+        const uint32_t m0 = (u_l == t0 % F) ? ~0u : 0u;
+        const uint32_t m1 = (u_l == t1 % F) ? ~0u : 0u;
+        p_hi = as_bf(v4u{h01 & m0, h23 & m0, h01 & m1, h23 & m1});
+        p_lo = as_bf(v4u{l01 & m0, l23 & m0, l01 & m1, l23 & m1});
+      }
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const uint32_t na = v_bf16_low_bytes<BITS>(c[u0].v, m, c80);
-        const uint32_t nb = v_bf16_low_bytes<BITS>(c[u1].v, m, c80);
+        const uint32_t na = v_bf16_low_bytes<BITS>(c[t0].v, m, c80);
+        const uint32_t nb = v_bf16_low_bytes<BITS>(c[t1].v, m, c80);
         const v8bf vb = as_bf(v4u{bias_bf16_lo<BITS>(na), bias_bf16_hi<BITS>(na), bias_bf16_lo<BITS>(nb),
                                   bias_bf16_hi<BITS>(nb)});
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc[m], 0, 0, 0);
       }
     }
-    // stage the next step's scale/zero blocks (loaded two steps ago) in the other buffer
+    // stage the next step's scale/zero blocks in the other buffer
 #pragma unroll
     for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[buf ^ 1][u])[lane] = next[u].sz;
     wave_lds_sync();
@@ -610,75 +669,109 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     }
   };
 
-  // Triple-buffered walk: while the tiles of one buffer are processed, the next two steps'
-  // tiles are already loading (about two steps of latency covered).
-  // Step k reads scale/zero buffer k & 1; the six-step cycle keeps the parity aligned.
 #pragma unroll
   for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[0][u])[lane] = x0[u].sz;
   wave_lds_sync();
-#if KVQ_DECODE_PREFETCH_STEPS == 3
-  // four buffers: while one step is processed the next three are loading
-  TileCodes x3[NT];
-  int64_t pg3[NT];
-  fetch(tile_begin + 2 * NT, x2, pg2);
-  for (int tile = tile_begin;; tile += 4 * NT) {
-    fetch(tile + 3 * NT, x3, pg3);
-    step(x0, pg0, tile, x1, 0);
-    if (tile + NT >= tile_end) break;
-    fetch(tile + 4 * NT, x0, pg0);
-    step(x1, pg1, tile + NT, x2, 1);
-    if (tile + 2 * NT >= tile_end) break;
-    fetch(tile + 5 * NT, x1, pg1);
-    step(x2, pg2, tile + 2 * NT, x3, 0);
-    if (tile + 3 * NT >= tile_end) break;
-    fetch(tile + 6 * NT, x2, pg2);
-    step(x3, pg3, tile + 3 * NT, x0, 1);
-    if (tile + 4 * NT >= tile_end) break;
+  if constexpr (NT >= 4) {
+    // Double-buffered walk: while one step's tiles are processed, the next step's are loading.
+    for (int tile = tile_begin;; tile += 2 * NT) {
+      step(x0, pg0, tile, x1, 0);
+      if (tile + NT >= tile_end) break;
+      fetch(tile + 2 * NT, x0, pg0);
+      step(x1, pg1, tile + NT, x0, 1);
+      if (tile + 2 * NT >= tile_end) break;
+      fetch(tile + 3 * NT, x1, pg1);
+    }
+  } else {
+    // Triple-buffered walk: while the tiles of one buffer are processed, the next two steps'
+    // tiles are already loading. Step k reads scale/zero buffer k & 1; the six-step cycle keeps
+    // the parity aligned.
+    TileCodes x2[NT];
+    int64_t pg2[NT];
+    for (int tile = tile_begin;; tile += 6 * NT) {
+      fetch(tile + 2 * NT, x2, pg2);
+      step(x0, pg0, tile, x1, 0);
+      if (tile + NT >= tile_end) break;
+      fetch(tile + 3 * NT, x0, pg0);
+      step(x1, pg1, tile + NT, x2, 1);
+      if (tile + 2 * NT >= tile_end) break;
+      fetch(tile + 4 * NT, x1, pg1);
+      step(x2, pg2, tile + 2 * NT, x0, 0);
+      if (tile + 3 * NT >= tile_end) break;
+      fetch(tile + 5 * NT, x2, pg2);
+      step(x0, pg0, tile + 3 * NT, x1, 1);
+      if (tile + 4 * NT >= tile_end) break;
+      fetch(tile + 6 * NT, x0, pg0);
+      step(x1, pg1, tile + 4 * NT, x2, 0);
+      if (tile + 5 * NT >= tile_end) break;
+      fetch(tile + 7 * NT, x1, pg1);
+      step(x2, pg2, tile + 5 * NT, x0, 1);
+      if (tile + 6 * NT >= tile_end) break;
+    }
   }
-#else
-  for (int tile = tile_begin;; tile += 6 * NT) {
-    fetch(tile + 2 * NT, x2, pg2);
-    step(x0, pg0, tile, x1, 0);
-    if (tile + NT >= tile_end) break;
-    fetch(tile + 3 * NT, x0, pg0);
-    step(x1, pg1, tile + NT, x2, 1);
-    if (tile + 2 * NT >= tile_end) break;
-    fetch(tile + 4 * NT, x1, pg1);
-    step(x2, pg2, tile + 2 * NT, x0, 0);
-    if (tile + 3 * NT >= tile_end) break;
-    fetch(tile + 5 * NT, x2, pg2);
-    step(x0, pg0, tile + 3 * NT, x1, 1);
-    if (tile + 4 * NT >= tile_end) break;
-    fetch(tile + 6 * NT, x0, pg0);
-    step(x1, pg1, tile + 4 * NT, x2, 0);
-    if (tile + 5 * NT >= tile_end) break;
-    fetch(tile + 7 * NT, x1, pg1);
-    step(x2, pg2, tile + 5 * NT, x0, 1);
-    if (tile + 6 * NT >= tile_end) break;
-  }
-#endif
 
-  // ---- finish: totals of head n, then moved to the accumulator rows (heads 4G+i)
+  // ---- finish: each head's totals over the row groups and the tile slots (then equal in every
+  // lane of the head; lane h < W holds head h)
   l_part += __shfl_xor(l_part, 16, 64);
   l_part += __shfl_xor(l_part, 32, 64);
   z_part += __shfl_xor(z_part, 16, 64);
   z_part += __shfl_xor(z_part, 32, 64);
-  float lrow[4], zrow[4], mrow[4];
+  if constexpr (F >= 2) {
+    l_part += row_ror<8>(l_part);
+    z_part += row_ror<8>(z_part);
+  }
+  if constexpr (F == 4) {
+    l_part += row_ror<4>(l_part);
+    z_part += row_ror<4>(z_part);
+  }
+  // S output heads per lane: F = 1: heads 4G + s, straight from the accumulator rows; F > 1:
+  // heads G + 4s, the sum of their F slot rows, exchanged through LDS.
+  constexpr int S = (F == 1) ? 4 : W / 4;
+  float ov[S][8];
+  int hh[S];
+  if constexpr (F == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lrow[i] = __shfl(l_part, 4 * G + i, 64);
-    zrow[i] = __shfl(z_part, 4 * G + i, 64);
-    mrow[i] = __shfl(m_run, 4 * G + i, 64);
+    for (int s = 0; s < S; ++s) {
+      hh[s] = 4 * G + s;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ov[s][m] = acc[m][s];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[4 * G + i][2 * n] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      red[4 * G + i][2 * n + 1] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      hh[s] = G + 4 * s;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) ov[s][m] = 0.f;
+#pragma unroll
+      for (int u = 0; u < F; ++u) {
+        const float4 ra = red[u * W + hh[s]][2 * n], rb = red[u * W + hh[s]][2 * n + 1];
+        ov[s][0] += ra.x; ov[s][1] += ra.y; ov[s][2] += ra.z; ov[s][3] += ra.w;
+        ov[s][4] += rb.x; ov[s][5] += rb.y; ov[s][6] += rb.z; ov[s][7] += rb.w;
+      }
+    }
+  }
+  float lrow[S], zrow[S], mrow[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    lrow[s] = __shfl(l_part, hh[s], 64);
+    zrow[s] = __shfl(z_part, hh[s], 64);
+    mrow[s] = __shfl(m_run, hh[s], 64);
   }
 
   if (a.num_splits == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 4 * G + i;
+    for (int s = 0; s < S; ++s) {
+      const int c = hh[s];
       float o[8];
-      const float inv_l = (lrow[i] > 0.f) ? 1.0f / lrow[i] : 0.f;
+      const float inv_l = (lrow[s] > 0.f) ? 1.0f / lrow[s] : 0.f;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[m] = (c < ncols) ? (acc[m][i] + zrow[i]) * inv_l : 0.f;
+      for (int m = 0; m < 8; ++m) o[m] = (c < ncols) ? (ov[s][m] + zrow[s]) * inv_l : 0.f;
       fwht_row16_planned(o, a.rot, lf);  // R^T = R: back to the original basis
       if (c < ncols_rows) {
         float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf.pos);
@@ -693,14 +786,15 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // maximum and sum) for the merge kernel.
   const int64_t pairs = static_cast<int64_t>(a.batch) * (MQ ? a.q_len_max : 1) * a.num_q_heads;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * G + i;
+  for (int s = 0; s < S; ++s) {
+    const int c = hh[s];
     if (c < ncols) {
       const int64_t row = split * pairs + col_row(c);
       float4* dst = reinterpret_cast<float4*>(a.ws_acc + row * kHeadDim + 8 * n);
-      dst[0] = make_float4(acc[0][i] + zrow[i], acc[1][i] + zrow[i], acc[2][i] + zrow[i], acc[3][i] + zrow[i]);
-      dst[1] = make_float4(acc[4][i] + zrow[i], acc[5][i] + zrow[i], acc[6][i] + zrow[i], acc[7][i] + zrow[i]);
-      if (n == 0) reinterpret_cast<float2*>(a.ws_ml)[row] = make_float2(mrow[i], lrow[i]);
+      const float zr = zrow[s];
+      dst[0] = make_float4(ov[s][0] + zr, ov[s][1] + zr, ov[s][2] + zr, ov[s][3] + zr);
+      dst[1] = make_float4(ov[s][4] + zr, ov[s][5] + zr, ov[s][6] + zr, ov[s][7] + zr);
+      if (n == 0) reinterpret_cast<float2*>(a.ws_ml)[row] = make_float2(mrow[s], lrow[s]);
     }
   }
 }
@@ -785,16 +879,15 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   }
 }
 
-template <bool MQ>
+template <bool MQ, int F, int NT>
 hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const bool ps16 = a.page_size == 16;
-  constexpr int kNT = KVQ_DECODE_STEP_TILES;
   if (a.bits == 4) {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, kNT, MQ>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, kNT, MQ>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, NT, MQ, F>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, NT, MQ, F>), grid, dim3(64), 0, stream, a);
   } else {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, kNT, MQ>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, kNT, MQ>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, NT, MQ, F>), grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, NT, MQ, F>), grid, dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -808,7 +901,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const unsigned tiles = a.q_lens ? static_cast<unsigned>(mq_column_tiles(a.q_len_max, a.num_q_heads / a.num_kv_heads)) : 1u;
   const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
                   static_cast<unsigned>(a.batch));
-  hipError_t e = a.q_lens ? launch_kernel<true>(a, grid, stream) : launch_kernel<false>(a, grid, stream);
+  hipError_t e;
+  const int g = a.num_q_heads / a.num_kv_heads;
+  if (a.q_lens) {
+    e = launch_kernel<true, 1, 2>(a, grid, stream);
+  } else if constexpr (KVQ_DECODE_PACK >= 4) {
+    e = (g <= 4) ? launch_kernel<false, 4, 4>(a, grid, stream) : launch_kernel<false, 2, 2>(a, grid, stream);
+  } else if constexpr (KVQ_DECODE_PACK == 2) {
+    e = launch_kernel<false, 2, 2>(a, grid, stream);  // g <= 8 (checked by the caller)
+  } else {
+    e = launch_kernel<false, 1, 2>(a, grid, stream);
+  }
   if (e != hipSuccess || a.num_splits == 1) return e;
   return launch_decode_merge(a, stream);
 }
