@@ -38,8 +38,8 @@ N_CACHE_COPIES = 14
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="llama3_8b")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-iters", type=int, default=200, help="extra decode-only launches for the decode roofline")
