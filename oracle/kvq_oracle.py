@@ -22,6 +22,11 @@ It is the plain definition of what the method computes, written out slowly with 
 * Several queries per sequence (chunked prefill, speculative verification) -- the same attention
   with a causal limit per query: the paged low-bit attention of the OSCAR abstract applied to the
   prefill side.
+* Per-channel pages (``PagedCachePC``, ``write_pages_pc``, ``decode_pc``) -- the per-channel
+  reading of OScaR (OScaR abstract on the openalex page: "advancing the per-channel paradigm";
+  zhichai.net summary, "Root Cause: Token Norm Imbalance" and "The OScaR Framework"): per-token
+  scaling after the rotation, then one (scale, zero) per channel shared by the tokens of a page;
+  a sequence's unfinished last page stays in bf16 until it is complete.
 * Baseline -- attention over an unquantized bf16 paged cache (``PagedCacheBF16``,
   ``append_bf16``, ``decode_bf16``): the BF16 split decode the OScaR abstract (thelatestinai.com
   page) measures its speed-up against, used to put the low-bit path's speed next to it.
@@ -67,6 +72,7 @@ __all__ = [
     "rotate_quantize", "pack_rows", "unpack_rows", "PagedCache", "append",
     "gather_sequence", "attend", "decode", "dequant_page", "bf16_to_f32",
     "PagedCacheBF16", "append_bf16", "decode_bf16", "multi_query_attention",
+    "quantize_channels", "PagedCachePC", "quantize_page_pc", "write_pages_pc", "dequant_page_pc", "decode_pc",
 ]
 
 
@@ -420,4 +426,159 @@ def decode_bf16(cache: PagedCacheBF16, q_bits: np.ndarray, block_table: np.ndarr
             ks[j] = bf16_to_f32(kr)
             vs[j] = bf16_to_f32(vr)
         out[b, h] = attend(bf16_to_f32(q_bits[b, h]), ks, vs, scale).astype(np.float32)
+    return out
+
+
+# ----------------------------------------------------------------------------- per-channel pages
+# The per-channel reading of OScaR (OScaR abstract on the openalex page: rotation and per-token
+# scaling make the per-channel quantization paradigm work under extreme compression; zhichai.net
+# summary, "The OScaR Framework": V-hat = Quant(S (R V))). Each token is rotated (y = R x) and
+# divided by its own scale s (the token's RMS, as in the token-wise variant); the normalised tokens
+# u = y / s of one page then share one asymmetric (scale, zero) pair per channel. A page is
+# quantized once all its tokens exist; the tokens of a sequence's unfinished last page stay in
+# bf16 (the residual window) and are attended as they are.
+#
+# Layout (caller-owned arrays):
+#   K codes  [num_pages][kv_heads][page_size][row]          as in the token-wise cache
+#   V codes  [num_pages][kv_heads][page_size / 4][row][4]   as in the token-wise cache
+#   K/V s    float32 [num_pages][kv_heads][page_size]         per-token scale
+#   K/V cp   float32 [num_pages][kv_heads][2][head_dim]       {scale[d], zero[d]} per channel
+#   tail     bf16 bits [batch][page_size][kv_heads][head_dim] the residual window of each sequence
+
+
+def quantize_channels(u: np.ndarray, bits: int):
+    """Per-channel asymmetric quantization of float32 u [T, d] over its T tokens.
+
+    Returns (codes uint8 [T, d], scale float32 [d], zero float32 [d], t float64 [T, d]), t being
+    the pre-rounding value (u - min) / scale in float64 from the float32 operands. Same rule as
+    the token-wise quantizer, with the minimum and maximum taken down each channel.
+    """
+    u = np.asarray(u, dtype=np.float32)
+    qmax = np.float32(2 ** bits - 1)
+    mn = u.min(axis=0)
+    mx = u.max(axis=0)
+    scale = (mx - mn) / qmax                            # float32 subtract, IEEE divide
+    live = scale != 0
+    safe = np.where(live, scale, np.float32(1.0))
+    tf = (u - mn[None, :]) / safe[None, :]              # float32, IEEE divide
+    codes = np.clip(np.rint(tf), 0, qmax).astype(np.uint8)
+    codes[:, ~live] = 0
+    t = (u.astype(np.float64) - mn[None, :].astype(np.float64)) / safe[None, :].astype(np.float64)
+    t[:, ~live] = 0.0
+    return codes, scale.astype(np.float32), mn.astype(np.float32), t
+
+
+class PagedCachePC:
+    """Host copy of a per-channel cache (layout in the comment above)."""
+
+    def __init__(self, num_pages: int, kv_heads: int, page_size: int, head_dim: int, bits: int,
+                 poison: bool = True):
+        if page_size % 4:
+            raise ValueError("page_size must be a multiple of 4")
+        self.num_pages, self.kv_heads, self.page_size = num_pages, kv_heads, page_size
+        self.head_dim, self.bits = head_dim, bits
+        self.row = head_dim * bits // 8
+        fill = 0xAA if poison else 0
+        f_fill = np.nan if poison else 0.0
+        self.k_codes = np.full((num_pages, kv_heads, page_size, self.row), fill, dtype=np.uint8)
+        self.v_codes = np.full((num_pages, kv_heads, page_size // 4, self.row, 4), fill, dtype=np.uint8)
+        self.k_s = np.full((num_pages, kv_heads, page_size), f_fill, dtype=np.float32)
+        self.v_s = np.full((num_pages, kv_heads, page_size), f_fill, dtype=np.float32)
+        self.k_cp = np.full((num_pages, kv_heads, 2, head_dim), f_fill, dtype=np.float32)
+        self.v_cp = np.full((num_pages, kv_heads, 2, head_dim), f_fill, dtype=np.float32)
+
+    def write_page(self, page: int, head: int, kc, ks, kcp, vc, vs, vcp):
+        """Codes [ps, d], token scales [ps] and (scale, zero) [2, d] of K and V of one page-head."""
+        kp = pack_rows(kc, self.bits)
+        vp = pack_rows(vc, self.bits)
+        self.k_codes[page, head] = kp
+        for t in range(self.page_size):
+            self.v_codes[page, head, t // 4, :, t % 4] = vp[t]
+        self.k_s[page, head] = ks
+        self.v_s[page, head] = vs
+        self.k_cp[page, head] = kcp
+        self.v_cp[page, head] = vcp
+
+    def read_page(self, page: int, head: int, tensor: str):
+        """(codes uint8 [ps, d], token scales [ps], (scale, zero) [2, d]) of one page-head."""
+        if tensor == "k":
+            packed = self.k_codes[page, head]
+            return unpack_rows(packed, self.bits), self.k_s[page, head], self.k_cp[page, head]
+        packed = self.v_codes[page, head].transpose(0, 2, 1).reshape(self.page_size, self.row)
+        return unpack_rows(packed, self.bits), self.v_s[page, head], self.v_cp[page, head]
+
+
+def quantize_page_pc(x_bits: np.ndarray, b: int, bits: int):
+    """One page-head of one tensor: bf16 bits [ps, d] -> (codes [ps, d], s [ps], cp [2, d], t).
+
+    y = R x per token (float32), s = RMS(y) per token, u = y / s (float32, IEEE divide), then the
+    per-channel quantizer over the page's tokens.
+    """
+    y = rotate_f32(bf16_to_f32(x_bits), b)
+    s = token_rms(y)
+    u = y / s[:, None]
+    codes, sc, zr, t = quantize_channels(u, bits)
+    return codes, s, np.stack([sc, zr]).astype(np.float32), t
+
+
+def write_pages_pc(cache: PagedCachePC, k_bits: np.ndarray, v_bits: np.ndarray, page_ids: np.ndarray,
+                   hadamard_block: int):
+    """Quantize whole pages: input page i is tokens i * ps .. i * ps + ps - 1 of k_bits / v_bits
+    ([n * ps, kv_heads, d] bf16 bits) and goes to cache page page_ids[i] (negative: skipped).
+    Returns the pre-rounding values {'k_t', 'v_t'} [n, kv_heads, ps, d] for boundary checks."""
+    ps, h_n, d = cache.page_size, cache.kv_heads, cache.head_dim
+    n = len(page_ids)
+    k_t = np.zeros((n, h_n, ps, d))
+    v_t = np.zeros((n, h_n, ps, d))
+    for i in range(n):
+        page = int(page_ids[i])
+        for h in range(h_n):
+            kc, ks, kcp, kt = quantize_page_pc(k_bits[i * ps:(i + 1) * ps, h], hadamard_block, cache.bits)
+            vc, vs, vcp, vt = quantize_page_pc(v_bits[i * ps:(i + 1) * ps, h], hadamard_block, cache.bits)
+            k_t[i, h], v_t[i, h] = kt, vt
+            if page >= 0:
+                cache.write_page(page, h, kc, ks, kcp, vc, vs, vcp)
+    return {"k_t": k_t, "v_t": v_t}
+
+
+def dequant_page_pc(cache: PagedCachePC, page: int, head: int, tensor: str) -> np.ndarray:
+    """float64 [ps, d] in the rotated basis: s_t (code * scale_c + zero_c)."""
+    codes, s, cp = cache.read_page(page, head, tensor)
+    u = codes.astype(np.float64) * cp[0].astype(np.float64)[None, :] + cp[1].astype(np.float64)[None, :]
+    return u * s.astype(np.float64)[:, None]
+
+
+def decode_pc(cache: PagedCachePC, q_bits: np.ndarray, block_table: np.ndarray, context_lens: np.ndarray,
+              tail_k_bits: np.ndarray, tail_v_bits: np.ndarray, num_kv_heads: int, hadamard_block: int,
+              softmax_scale: float = 0.0, heads=None) -> np.ndarray:
+    """Decode attention over a per-channel cache plus the residual window, float32 [B, Hq, d].
+
+    Sequence b of length L has L // ps complete pages (block_table[b][0 ..]) and L % ps tokens in
+    tail[b][0 ..]. The pages are dequantized and rotated back (R is its own inverse), the tail is
+    used as given; then softmax attention of the bf16 query over all L tokens.
+    """
+    bsz, hq, d = q_bits.shape
+    g = hq // num_kv_heads
+    ps = cache.page_size
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(d)
+    r = rotation_matrix(d, hadamard_block)
+    out = np.full((bsz, hq, d), np.nan, dtype=np.float32)
+    todo = heads if heads is not None else [(b, h) for b in range(bsz) for h in range(hq)]
+    cached = {}
+    for b, h in todo:
+        kvh = h // g
+        length = int(context_lens[b])
+        if (b, kvh) not in cached:
+            n_full, n_tail = length // ps, length % ps
+            ks, vs = [], []
+            for j in range(n_full):
+                page = int(block_table[b, j])
+                ks.append(dequant_page_pc(cache, page, kvh, "k") @ r)   # rows: (R k)^T R = k^T
+                vs.append(dequant_page_pc(cache, page, kvh, "v") @ r)
+            ks.append(bf16_to_f32(tail_k_bits[b, :n_tail, kvh]).astype(np.float64))
+            vs.append(bf16_to_f32(tail_v_bits[b, :n_tail, kvh]).astype(np.float64))
+            cached[(b, kvh)] = (np.concatenate(ks, axis=0), np.concatenate(vs, axis=0))
+        kk, vv = cached[(b, kvh)]
+        q = bf16_to_f32(q_bits[b, h]).astype(np.float64)
+        out[b, h] = attend(q, kk, vv, scale).astype(np.float32)
     return out

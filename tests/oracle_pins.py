@@ -559,4 +559,191 @@ def pin_decode_bf16_definition():
     assert np.allclose(out[1, 3], bf, rtol=1e-5, atol=1e-7)
 
 
+# ----------------------------------------------------------------------------- per-channel pages
+
+def pin_pc_channel_quantizer():
+    """Per-channel quantizer: the minimum and maximum are taken down each channel (a grid with
+    per-channel gains and offsets is recovered exactly), a two-token page puts every channel's
+    tokens on codes 0 and qmax, a constant channel gets scale 0, and the rounding error stays
+    within half a step of its own channel."""
+    rng = np.random.default_rng(21)
+    for bits in (2, 4):
+        qmax = 2 ** bits - 1
+        c = rng.integers(0, qmax + 1, size=(64, 128))
+        c[0], c[1] = 0, qmax                          # every channel reaches both ends
+        gain = np.float32(2.0) ** rng.integers(-6, 4, size=128).astype(np.float32)
+        off = rng.integers(-8, 8, size=128).astype(np.float32) / np.float32(4)
+        u = (c * gain[None, :] + off[None, :]).astype(np.float32)
+        codes, scale, zero, _ = O.quantize_channels(u, bits)
+        assert np.array_equal(codes, c.astype(np.uint8))
+        assert np.array_equal(scale, gain) and np.array_equal(zero, off)
+        # two tokens: per channel the smaller one gets 0, the larger qmax
+        two = rng.standard_normal((2, 128)).astype(np.float32)
+        codes, scale, zero, _ = O.quantize_channels(two, bits)
+        lo = two.argmin(axis=0)
+        assert np.all(codes[lo, np.arange(128)] == 0) and np.all(codes[1 - lo, np.arange(128)] == qmax)
+        assert np.array_equal(scale, (two.max(axis=0) - two.min(axis=0)) / np.float32(qmax))
+        # constant channel
+        u = rng.standard_normal((16, 128)).astype(np.float32)
+        u[:, 5] = np.float32(-0.75)
+        codes, scale, zero, _ = O.quantize_channels(u, bits)
+        assert scale[5] == 0 and zero[5] == np.float32(-0.75) and np.all(codes[:, 5] == 0)
+        # error bound of random data, per channel
+        u = (rng.standard_normal((128, 128)) * rng.lognormal(0, 1, size=(1, 128))).astype(np.float32)
+        codes, scale, zero, _ = O.quantize_channels(u, bits)
+        deq = codes * scale[None, :].astype(np.float64) + zero[None, :]
+        ulp = np.spacing(np.abs(u).max(axis=0, keepdims=True)).astype(np.float64)
+        assert np.all(np.abs(deq - u) <= scale[None, :] / 2 + 4 * ulp)
+
+
+def pin_pc_token_scale_equivariance():
+    """Omni-token scaling makes the page's codes blind to each token's norm: multiplying one token
+    by a power of two leaves every code and every channel (scale, zero) unchanged and multiplies
+    that token's stored scale by the same factor (all steps exact). Without the scaling the
+    small-norm tokens of a page with a wide norm spread would collapse onto one code; with it each
+    token's relative error is bounded by the channel steps of unit-RMS tokens."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((32, 128)).astype(np.float32)
+    xb = _bits(x)
+    for bits in (2, 4):
+        c0, s0, cp0, _ = O.quantize_page_pc(xb, 128, bits)
+        for t, a in ((3, 4.0), (17, 0.125), (31, 1024.0)):
+            x2 = x.copy()
+            x2[t] *= np.float32(a)
+            c1, s1, cp1, _ = O.quantize_page_pc(_bits(x2), 128, bits)
+            assert np.array_equal(c1, c0) and np.array_equal(cp1, cp0)
+            want = s0.copy()
+            want[t] *= np.float32(a)
+            assert np.array_equal(s1, want)
+        # norm spread of 1e6 across the page: every token keeps a bounded relative error
+        wide = (rng.standard_normal((64, 128)) * np.exp(rng.uniform(-7, 7, size=(64, 1)))).astype(np.float32)
+        wb = _bits(wide)
+        codes, s, cp, _ = O.quantize_page_pc(wb, 128, bits)
+        y = O.rotate_f32(O.bf16_to_f32(wb), 128).astype(np.float64)
+        deq = (codes * cp[0].astype(np.float64) + cp[1]) * s[:, None].astype(np.float64)
+        rel = np.linalg.norm(deq - y, axis=1) / np.linalg.norm(y, axis=1)
+        bound = np.sqrt(np.mean(cp[0].astype(np.float64) ** 2)) / 2 * 1.0001
+        assert np.all(rel <= bound), (bits, rel.max(), bound)
+
+
+def pin_pc_layout_matches_token_cache():
+    """The per-channel cache stores codes exactly where the token-wise cache does (so the two read
+    paths share their code loads), token scales per token and (scale, zero) per channel."""
+    rng = np.random.default_rng(23)
+    for bits in (2, 4):
+        ps = 32
+        pc = O.PagedCachePC(3, 2, ps, 128, bits)
+        tw = O.PagedCache(3, 2, ps, 128, bits)
+        kc = rng.integers(0, 2 ** bits, size=(ps, 128)).astype(np.uint8)
+        vc = rng.integers(0, 2 ** bits, size=(ps, 128)).astype(np.uint8)
+        ks, vs = rng.random(ps).astype(np.float32), rng.random(ps).astype(np.float32)
+        kcp, vcp = rng.random((2, 128)).astype(np.float32), rng.random((2, 128)).astype(np.float32)
+        pc.write_page(2, 1, kc, ks, kcp, vc, vs, vcp)
+        kp, vp = O.pack_rows(kc, bits), O.pack_rows(vc, bits)
+        for t in range(ps):
+            tw.write_token(2, t, 1, kp[t], 0.0, 0.0, vp[t], 0.0, 0.0)
+        assert np.array_equal(pc.k_codes, tw.k_codes) and np.array_equal(pc.v_codes, tw.v_codes)
+        for tensor, c, s, cp in (("k", kc, ks, kcp), ("v", vc, vs, vcp)):
+            rc, rs, rcp = pc.read_page(2, 1, tensor)
+            assert np.array_equal(rc, c) and np.array_equal(rs, s) and np.array_equal(rcp, cp)
+        assert np.all(np.isnan(pc.k_s[:2])) and np.all(np.isnan(pc.v_cp[2, 0]))
+
+
+def _pc_case(lens, ps, bits, hb, rng, exact):
+    """A per-channel cache holding the complete pages of sequences of the given lengths, their
+    tails, and the raw K/V of every token. exact: tokens +-a_t with a_t a power of two and both
+    signs in every channel of every page, so that (with hb = 1) each page is quantized exactly."""
+    h_n, d = 2, 128
+    n_pages_seq = [n // ps for n in lens]
+    bt = np.full((len(lens), max(1, max(n_pages_seq))), -1, dtype=np.int32)
+    order = rng.permutation(sum(n_pages_seq) + 2)
+    raw_k, raw_v = [], []
+    pages_k, pages_v, ids = [], [], []
+    tail_k = np.zeros((len(lens), ps, h_n, d), dtype=np.uint16)
+    tail_v = np.zeros((len(lens), ps, h_n, d), dtype=np.uint16)
+    nxt = 0
+    for b, n in enumerate(lens):
+        if exact:
+            sign = np.where(rng.random((n, h_n, d)) < 0.5, -1.0, 1.0)
+            for j in range(n // ps):
+                sign[j * ps, :, :], sign[j * ps + 1, :, :] = -1.0, 1.0
+            amp = np.float32(2.0) ** rng.integers(-3, 4, size=(n, h_n, 1))
+            k = (sign * amp).astype(np.float32)
+            v = (np.roll(sign, 1, axis=0) * amp[::-1]).astype(np.float32)
+        else:
+            k = (rng.standard_normal((n, h_n, d)) * rng.lognormal(0, 1, size=(n, h_n, 1))).astype(np.float32)
+            v = rng.standard_normal((n, h_n, d)).astype(np.float32)
+        kb, vb = _bits(k), _bits(v)
+        raw_k.append(O.bf16_to_f32(kb))
+        raw_v.append(O.bf16_to_f32(vb))
+        for j in range(n // ps):
+            bt[b, j] = order[nxt]
+            ids.append(order[nxt])
+            nxt += 1
+            pages_k.append(kb[j * ps:(j + 1) * ps])
+            pages_v.append(vb[j * ps:(j + 1) * ps])
+        full = (n // ps) * ps
+        tail_k[b, :n - full] = kb[full:]
+        tail_v[b, :n - full] = vb[full:]
+    cache = O.PagedCachePC(len(order), h_n, ps, d, bits)
+    if ids:
+        O.write_pages_pc(cache, np.concatenate(pages_k), np.concatenate(pages_v), np.array(ids), hb)
+    return cache, bt, tail_k, tail_v, raw_k, raw_v
+
+
+def pin_pc_decode_definition():
+    """Decode over per-channel pages plus the residual window is softmax attention over every
+    token of the sequence: exact (up to the float32 rounding of the step) when each page's
+    tokens sit on its quantization grid, for
+    sequences with only a tail, only complete pages, both, and none; close to the dense attention
+    (within the quantization error) for random data with the rotation."""
+    import torch
+    rng = np.random.default_rng(24)
+    ps = 32
+    lens = [0, 7, 64, 77, 32]
+    for bits in (2, 4):
+        cache, bt, tk, tv, rk, rv = _pc_case(lens, ps, bits, 1, rng, exact=True)
+        q = _bits(rng.standard_normal((len(lens), 4, 128)))
+        out = O.decode_pc(cache, q, bt, np.array(lens), tk, tv, 2, 1)
+        assert np.all(out[0] == 0)
+        for b, n in enumerate(lens):
+            if n == 0:
+                continue
+            for h in range(4):
+                qq = torch.from_numpy(O.bf16_to_f32(q[b, h]).astype(np.float64))[None, None, None]
+                kk = torch.from_numpy(rk[b][:, h // 2].astype(np.float64))[None, None]
+                vv = torch.from_numpy(rv[b][:, h // 2].astype(np.float64))[None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[0, 0, 0].numpy()
+                # the step 2 / qmax is not exact in float32: about 3e-8 relative per key
+                assert np.allclose(out[b, h], ref, rtol=2e-5, atol=2e-5 * np.abs(ref).max()), (bits, b, h)
+    # random data, real rotation: the same as attention over keys and values rebuilt by hand from
+    # the cache arrays (codes unpacked with shifts, scipy's Hadamard matrix for the rotation)
+    import scipy.linalg
+    lens = [96, 45]
+    cache, bt, tk, tv, rk, rv = _pc_case(lens, ps, 4, 128, rng, exact=False)
+    q = _bits(rng.standard_normal((2, 4, 128)))
+    out = O.decode_pc(cache, q, bt, np.array(lens), tk, tv, 2, 128)
+    rot = scipy.linalg.hadamard(128).astype(np.float64) / math.sqrt(128)
+    for b, n in enumerate(lens):
+        for kvh in range(2):
+            ks, vs = [], []
+            for j in range(n // ps):
+                pg = bt[b, j]
+                kbyte = cache.k_codes[pg, kvh].astype(np.int64)                      # [ps, 64]
+                kcode = np.stack([kbyte & 15, kbyte >> 4], axis=-1).reshape(ps, 128)
+                vbyte = cache.v_codes[pg, kvh].transpose(0, 2, 1).reshape(ps, 64).astype(np.int64)
+                vcode = np.stack([vbyte & 15, vbyte >> 4], axis=-1).reshape(ps, 128)
+                for code, sc, cp, acc in ((kcode, cache.k_s, cache.k_cp, ks), (vcode, cache.v_s, cache.v_cp, vs)):
+                    u = code * cp[pg, kvh, 0].astype(np.float64) + cp[pg, kvh, 1].astype(np.float64)
+                    acc.append((u * sc[pg, kvh][:, None].astype(np.float64)) @ rot)
+            full = (n // ps) * ps
+            ks.append(O.bf16_to_f32(tk[b, :n - full, kvh]).astype(np.float64))
+            vs.append(O.bf16_to_f32(tv[b, :n - full, kvh]).astype(np.float64))
+            kk = torch.from_numpy(np.concatenate(ks))[None, None]
+            vv = torch.from_numpy(np.concatenate(vs))[None, None]
+            for h in (2 * kvh, 2 * kvh + 1):
+                qq = torch.from_numpy(O.bf16_to_f32(q[b, h]).astype(np.float64))[None, None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[0, 0, 0].numpy()
+                assert np.allclose(out[b, h], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max()), (b, h)
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

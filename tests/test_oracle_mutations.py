@@ -205,9 +205,51 @@ def m_mq_off_by_one(mp):
     mp.setattr(O, "multi_query_attention", bad)
 
 
+def m_pc_token_axis(mp):
+    # the page quantized token by token (the token-wise quantizer) instead of channel by channel
+    mp.setattr(O, "quantize_channels", lambda u, bits: _real_quantize(u, bits))
+
+
+def m_pc_no_token_scale(mp):
+    real = O.quantize_page_pc
+
+    def bad(x_bits, b, bits):
+        y = O.rotate_f32(O.bf16_to_f32(x_bits), b)
+        codes, sc, zr, t = O.quantize_channels(y, bits)              # the scaling step left out
+        return codes, np.ones(len(y), np.float32), np.stack([sc, zr]).astype(np.float32), t
+    mp.setattr(O, "quantize_page_pc", bad)
+
+
+def m_pc_dequant_without_s(mp):
+    def bad(cache, page, head, tensor):
+        codes, s, cp = cache.read_page(page, head, tensor)
+        return codes.astype(np.float64) * cp[0].astype(np.float64)[None, :] + cp[1].astype(np.float64)[None, :]
+    mp.setattr(O, "dequant_page_pc", bad)
+
+
+def m_pc_tail_off_by_one(mp):
+    real = O.decode_pc
+
+    def bad(cache, q_bits, block_table, context_lens, tail_k_bits, tail_v_bits, num_kv_heads, hadamard_block,
+            softmax_scale=0.0, heads=None):
+        return real(cache, q_bits, block_table, context_lens, np.roll(tail_k_bits, 1, axis=1), tail_v_bits,
+                    num_kv_heads, hadamard_block, softmax_scale, heads)
+    mp.setattr(O, "decode_pc", bad)
+
+
+def m_pc_v_token_major(mp):
+    def write_page(self, page, head, kc, ks, kcp, vc, vs, vcp):
+        self.k_codes[page, head] = O.pack_rows(kc, self.bits)
+        self.v_codes[page, head] = O.pack_rows(vc, self.bits).reshape(self.page_size // 4, 4, self.row).transpose(0, 1, 2).reshape(self.page_size // 4, self.row, 4)
+        self.k_s[page, head], self.v_s[page, head] = ks, vs
+        self.k_cp[page, head], self.v_cp[page, head] = kcp, vcp
+    mp.setattr(O.PagedCachePC, "write_page", write_page)
+
+
 MUTATIONS = [m_hadamard_sign, m_hadamard_row_order, m_rotation_norm, m_round_half_up, m_qmax_off_by_one,
              m_zero_is_max, m_pack_high_first, m_v_interleave_swapped, m_no_softmax_scale,
-             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo, m_mq_off_by_one]
+             m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo, m_mq_off_by_one,
+             m_pc_token_axis, m_pc_no_token_scale, m_pc_dequant_without_s, m_pc_tail_off_by_one, m_pc_v_token_major]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
