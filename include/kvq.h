@@ -263,6 +263,62 @@ kvq_status kvq_paged_decode_attention_bf16(
     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
     float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
 
+/*
+ * Per-channel pages - the per-channel reading of OScaR (OScaR abstract on the openalex page: the
+ * rotation and a per-token scaling make per-channel quantization hold up at INT2; zhichai.net
+ * "OScaR: Occam's Razor for Extreme KV Cache Quantization in LLMs", sections "Root Cause: Token
+ * Norm Imbalance" and "The OScaR Framework", V-hat = Quant(S (R V))). Each token is rotated,
+ * y = R x, and divided by its RMS s (1 if 0): u = y / s. The page_size tokens of one page and KV
+ * head then share one asymmetric (scale, zero) per channel c over their u:
+ *   scale_c = (max_t u_tc - min_t u_tc) / (2^bits - 1), zero_c = min_t u_tc,
+ *   code_tc = clamp(rint((u_tc - zero_c) / scale_c), 0, 2^bits - 1)   (0 where scale_c = 0),
+ * and dequant = s_t (code_tc * scale_c + zero_c) in the rotated basis. A page is quantized once all
+ * its tokens exist; until then they stay in bf16 in the caller's residual window (tail).
+ *
+ * Layout (caller-owned device memory, row = head_dim * bits / 8 bytes):
+ *   K codes, V codes   as the token-wise cache (see the top of this file)
+ *   k_s, v_s           float [num_pages][num_kv_heads][page_size]         per-token s
+ *   k_cp, v_cp         float [num_pages][num_kv_heads][2][head_dim]       {scale[head_dim], zero[head_dim]}
+ *   tail_k, tail_v     bf16 [batch][page_size][num_kv_heads][head_dim]    sequence b's newest
+ *                      context_lens[b] % page_size tokens, oldest first
+ * page_size must be 32 or 64 (KVQ_ERR_UNSUPPORTED otherwise). Alignment: k, v, codes, k_cp, v_cp,
+ * tail_k, tail_v, q, out 16 bytes; k_s, v_s, page_ids, block_table, context_lens 4.
+ */
+
+/* Quantize whole pages: input page i is tokens i * page_size .. i * page_size + page_size - 1 of
+ * k and v (bf16 [num_input_pages * page_size][num_kv_heads][head_dim], token strides as for
+ * kvq_rotate_quantize_append) and is written to cache page page_ids[i] (int32 [num_input_pages]);
+ * ids outside [0, num_pages) are skipped, and two inputs with the same id race. Writes the codes,
+ * s and (scale, zero) of every KV head of those pages. num_input_pages == 0 is a no-op. */
+kvq_status kvq_pc_write_pages(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int32_t num_input_pages, const int32_t* page_ids, int32_t num_kv_heads, int32_t head_dim,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_s, float* v_s, float* k_cp, float* v_cp,
+    int32_t num_pages, int32_t page_size, int32_t hadamard_block, int32_t bits, hipStream_t stream);
+
+/* Workspace bytes of kvq_pc_decode_attention (never 0 for batch > 0; same arguments). */
+size_t kvq_pc_decode_workspace_size(
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t page_size, int32_t pages_per_split);
+
+/* Decode attention over per-channel pages and the residual window: sequence b attends to its
+ * context_lens[b] / page_size complete pages (block_table[b][0 ..], only those entries are read)
+ * followed by its context_lens[b] % page_size tail tokens. q bf16 [batch][num_q_heads][head_dim]
+ * (un-rotated; the kernel rotates it), at most 8 query heads per KV head; out float32
+ * [batch][num_q_heads][head_dim] in the original basis; a sequence of length 0 gives zeros. The
+ * workspace (kvq_pc_decode_workspace_size bytes) is required; its contents on entry do not
+ * matter. Other arguments as for kvq_paged_decode_attention. */
+kvq_status kvq_pc_decode_attention(
+    const uint16_t* q,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_s, const float* v_s,
+    const float* k_cp, const float* v_cp, int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    const uint16_t* tail_k, const uint16_t* tail_v,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,7 +72,8 @@ __all__ = [
     "rotate_quantize", "pack_rows", "unpack_rows", "PagedCache", "append",
     "gather_sequence", "attend", "decode", "dequant_page", "bf16_to_f32",
     "PagedCacheBF16", "append_bf16", "decode_bf16", "multi_query_attention",
-    "quantize_channels", "PagedCachePC", "quantize_page_pc", "write_pages_pc", "dequant_page_pc", "decode_pc",
+    "quantize_channels", "PagedCachePC", "quantize_page_pc", "quantize_rotated_page_pc", "write_pages_pc",
+    "dequant_page_pc", "decode_pc",
 ]
 
 
@@ -514,7 +515,11 @@ def quantize_page_pc(x_bits: np.ndarray, b: int, bits: int):
     y = R x per token (float32), s = RMS(y) per token, u = y / s (float32, IEEE divide), then the
     per-channel quantizer over the page's tokens.
     """
-    y = rotate_f32(bf16_to_f32(x_bits), b)
+    return quantize_rotated_page_pc(rotate_f32(bf16_to_f32(x_bits), b), bits)
+
+
+def quantize_rotated_page_pc(y: np.ndarray, bits: int):
+    """``quantize_page_pc`` from the rotated tokens y (float32 [ps, d]) on."""
     s = token_rms(y)
     u = y / s[:, None]
     codes, sc, zr, t = quantize_channels(u, bits)
@@ -530,11 +535,14 @@ def write_pages_pc(cache: PagedCachePC, k_bits: np.ndarray, v_bits: np.ndarray, 
     n = len(page_ids)
     k_t = np.zeros((n, h_n, ps, d))
     v_t = np.zeros((n, h_n, ps, d))
+    # every token rotated in one pass (rows are independent), then page by page
+    yk = rotate_f32(bf16_to_f32(k_bits[:n * ps].reshape(-1, d)), hadamard_block).reshape(n, ps, h_n, d)
+    yv = rotate_f32(bf16_to_f32(v_bits[:n * ps].reshape(-1, d)), hadamard_block).reshape(n, ps, h_n, d)
     for i in range(n):
         page = int(page_ids[i])
         for h in range(h_n):
-            kc, ks, kcp, kt = quantize_page_pc(k_bits[i * ps:(i + 1) * ps, h], hadamard_block, cache.bits)
-            vc, vs, vcp, vt = quantize_page_pc(v_bits[i * ps:(i + 1) * ps, h], hadamard_block, cache.bits)
+            kc, ks, kcp, kt = quantize_rotated_page_pc(yk[i, :, h], cache.bits)
+            vc, vs, vcp, vt = quantize_rotated_page_pc(yv[i, :, h], cache.bits)
             k_t[i, h], v_t[i, h] = kt, vt
             if page >= 0:
                 cache.write_page(page, h, kc, ks, kcp, vc, vs, vcp)

@@ -26,7 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_dequant.hip",
-           "kvq_baseline_bf16.hip"]
+           "kvq_baseline_bf16.hip", "kvq_pc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [

@@ -482,3 +482,132 @@ kvq_status kvq_paged_decode_attention_bf16(
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------- per-channel pages
+
+namespace {
+
+kvq_status check_pc(int32_t head_dim, int32_t page_size, int32_t hadamard_block, int32_t bits) {
+  if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
+  if (page_size != 32 && page_size != kvq::kPcMaxPage) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+// Page splits over the complete pages, plus the split of the unfinished page.
+kvq::SplitPlan pc_plan(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,
+                       int32_t pages_per_split) {
+  const int32_t full_tokens = max_context_len / page_size * page_size;
+  return kvq::plan_splits(batch, num_kv_heads, full_tokens, page_size, pages_per_split);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_pc_write_pages(
+    const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
+    int32_t num_input_pages, const int32_t* page_ids, int32_t num_kv_heads, int32_t head_dim,
+    uint8_t* k_codes, uint8_t* v_codes, float* k_s, float* v_s, float* k_cp, float* v_cp,
+    int32_t num_pages, int32_t page_size, int32_t hadamard_block, int32_t bits, hipStream_t stream) {
+  if (num_input_pages < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
+  if (kvq_status s = check_pc(head_dim, page_size, hadamard_block, bits)) return s;
+  if (num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (k_token_stride < row_elems || v_token_stride < row_elems || k_token_stride % 8 || v_token_stride % 8)
+    return KVQ_ERR_SHAPE;
+  if (num_input_pages == 0) return KVQ_OK;
+  if (!k || !v || !page_ids || !k_codes || !v_codes || !k_s || !v_s || !k_cp || !v_cp) return KVQ_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(page_ids, 4) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+      !aligned(k_s, 4) || !aligned(v_s, 4) || !aligned(k_cp, 16) || !aligned(v_cp, 16))
+    return KVQ_ERR_SHAPE;
+  kvq::PcWriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.k_stride = k_token_stride;
+  a.v_stride = v_token_stride;
+  a.num_input_pages = num_input_pages;
+  a.page_ids = page_ids;
+  a.num_kv_heads = num_kv_heads;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_s = k_s;
+  a.v_s = v_s;
+  a.k_cp = k_cp;
+  a.v_cp = v_cp;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  a.rot = kvq::make_row_fwht_plan(hadamard_block);
+  a.bits = bits;
+  return kvq::launch_pc_write(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_pc_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t page_size, int32_t pages_per_split) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kvq::kHeadDim || page_size <= 0 ||
+      max_context_len < 0 || pages_per_split < 0)
+    return 0;
+  const kvq::SplitPlan p = pc_plan(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  return workspace_layout(p.num_splits + 1, batch, num_q_heads).total;
+}
+
+kvq_status kvq_pc_decode_attention(
+    const uint16_t* q,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_s, const float* v_s,
+    const float* k_cp, const float* v_cp, int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    const uint16_t* tail_k, const uint16_t* tail_v,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream) {
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
+      max_pages_per_seq < 0 || pages_per_split < 0)
+    return KVQ_ERR_SHAPE;
+  if (kvq_status s = check_pc(head_dim, page_size, hadamard_block, bits)) return s;
+  if (num_q_heads % num_kv_heads) return KVQ_ERR_SHAPE;
+  if (num_q_heads / num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (max_pages_per_seq < max_context_len / page_size) return KVQ_ERR_SHAPE;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !k_codes || !v_codes || !k_s || !v_s || !k_cp || !v_cp || !block_table || !context_lens || !tail_k ||
+      !tail_v || !out)
+    return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_s, 4) ||
+      !aligned(v_s, 4) || !aligned(k_cp, 16) || !aligned(v_cp, 16) || !aligned(block_table, 4) ||
+      !aligned(context_lens, 4) || !aligned(tail_k, 16) || !aligned(tail_v, 16))
+    return KVQ_ERR_SHAPE;
+  const kvq::SplitPlan plan = pc_plan(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const WorkspaceLayout ws = workspace_layout(plan.num_splits + 1, batch, num_q_heads);
+  if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
+  kvq::PcDecodeArgs a{};
+  a.q = q;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_s = k_s;
+  a.v_s = v_s;
+  a.k_cp = k_cp;
+  a.v_cp = v_cp;
+  a.page_size = page_size;
+  a.block_table = block_table;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_pages = num_pages;
+  a.tail_k = tail_k;
+  a.tail_v = tail_v;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.rot = kvq::make_row_fwht_plan(hadamard_block);
+  a.bits = bits;
+  const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
+  a.qk_scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  a.num_splits = plan.num_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset);
+  a.out = out;
+  return kvq::launch_pc_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -88,7 +88,62 @@ struct DecodeArgs {
   uint8_t* v_codes_w;
   float* k_sz_w;
   float* v_sz_w;
+  // Merge: every split of every row holds a partial (an empty one has maximum -inf), instead of
+  // the splits that cover the row's pages.
+  int32_t all_splits;
 };
+
+// Per-channel pages (the per-channel reading of OScaR): codes as in the token-wise cache, a
+// float32 scale per token, a float32 (scale, zero) per channel per page-head.
+constexpr int kPcMaxPage = 64;    // page sizes 32 and 64
+
+struct PcWriteArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_stride, v_stride;     // elements between tokens
+  int32_t num_input_pages;        // input page i = tokens i * page_size .. + page_size - 1
+  const int32_t* page_ids;        // destination page of input page i (out of range: skipped)
+  int32_t num_kv_heads;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_s;                     // [num_pages][num_kv_heads][page_size]
+  float* v_s;
+  float* k_cp;                    // [num_pages][num_kv_heads][2][128] = {scale[128], zero[128]}
+  float* v_cp;
+  int32_t num_pages;
+  int32_t page_size;
+  RowFwhtPlan rot;
+  int32_t bits;
+};
+
+struct PcDecodeArgs {
+  const uint16_t* q;              // bf16 [batch][num_q_heads][128]
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const float* k_s;
+  const float* v_s;
+  const float* k_cp;
+  const float* v_cp;
+  int32_t page_size;
+  const int32_t* block_table;     // complete pages of each sequence
+  int32_t max_pages_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  int32_t num_pages;
+  const uint16_t* tail_k;         // bf16 [batch][page_size][num_kv_heads][128]: the unfinished page
+  const uint16_t* tail_v;
+  int32_t batch, num_q_heads, num_kv_heads;
+  RowFwhtPlan rot;
+  int32_t bits;
+  float qk_scale_log2;
+  int32_t num_splits;             // page splits; split num_splits attends the tail
+  int32_t pages_per_split;
+  float* ws_acc;                  // [num_splits + 1][batch][num_q_heads][128], original basis
+  float* ws_ml;
+  float* out;
+};
+hipError_t launch_pc_write(const PcWriteArgs& a, hipStream_t stream);
+hipError_t launch_pc_decode(const PcDecodeArgs& a, hipStream_t stream);
 
 struct DequantArgs {
   const uint8_t* codes;

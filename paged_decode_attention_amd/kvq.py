@@ -20,7 +20,8 @@ KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
            "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page",
            "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step",
-           "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention")
+           "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention", "kvq_pc_write_pages",
+           "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention")
 
 
 class KVQError(RuntimeError):
@@ -72,6 +73,15 @@ def lib() -> ctypes.CDLL:
     L.kvq_paged_decode_attention_bf16.restype = _i32
     L.kvq_paged_decode_attention_bf16.argtypes = [
         _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz, _i32, _p]
+    L.kvq_pc_write_pages.restype = _i32
+    L.kvq_pc_write_pages.argtypes = [
+        _p, _p, _i64, _i64, _i32, _p, _i32, _i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]
+    L.kvq_pc_decode_workspace_size.restype = _sz
+    L.kvq_pc_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    L.kvq_pc_decode_attention.restype = _i32
+    L.kvq_pc_decode_attention.argtypes = [
+        _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        _p, _p, _sz, _i32, _p]
     _lib = L
     return L
 
@@ -405,4 +415,122 @@ def paged_decode_attention_bf16(q: torch.Tensor, cache: PagedKVCacheBF16, block_
         _dev(context_lens, "context_lens", torch.int32), max_context_len, bsz, hq, cache.num_kv_heads, HEAD_DIM,
         float(softmax_scale), _dev(out, "out", torch.float32), ws_ptr, ws_bytes, pages_per_split, _stream(stream))
     _check(st, "kvq_paged_decode_attention_bf16")
+    return out
+
+
+# ----------------------------------------------------------------------------- per-channel pages
+
+@dataclass
+class PagedKVCachePC:
+    """Per-channel cache of the OScaR per-channel reading (six device tensors): codes as in
+    ``PagedKVCache``, a float32 scale per token and a float32 (scale, zero) per channel per page-head."""
+    k_codes: torch.Tensor   # uint8 [P, H, ps, row]
+    v_codes: torch.Tensor   # uint8 [P, H, ps/4, row, 4]
+    k_s: torch.Tensor       # float32 [P, H, ps]
+    v_s: torch.Tensor       # float32 [P, H, ps]
+    k_cp: torch.Tensor      # float32 [P, H, 2, 128] = {scale[128], zero[128]}
+    v_cp: torch.Tensor      # float32 [P, H, 2, 128]
+    bits: int
+
+    @staticmethod
+    def empty(num_pages: int, num_kv_heads: int, page_size: int, bits: int, device="cuda") -> "PagedKVCachePC":
+        row = HEAD_DIM * bits // 8
+        u8, f32 = torch.uint8, torch.float32
+        return PagedKVCachePC(
+            torch.empty((num_pages, num_kv_heads, page_size, row), dtype=u8, device=device),
+            torch.empty((num_pages, num_kv_heads, page_size // 4, row, 4), dtype=u8, device=device),
+            torch.empty((num_pages, num_kv_heads, page_size), dtype=f32, device=device),
+            torch.empty((num_pages, num_kv_heads, page_size), dtype=f32, device=device),
+            torch.empty((num_pages, num_kv_heads, 2, HEAD_DIM), dtype=f32, device=device),
+            torch.empty((num_pages, num_kv_heads, 2, HEAD_DIM), dtype=f32, device=device), bits)
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_codes.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_codes.shape[1]
+
+    @property
+    def page_size(self) -> int:
+        return self.k_codes.shape[2]
+
+    def _check_layout(self):
+        p, h, ps, row = self.k_codes.shape
+        if row != HEAD_DIM * self.bits // 8 or tuple(self.v_codes.shape) != (p, h, ps // 4, row, 4) \
+                or tuple(self.k_s.shape) != (p, h, ps) or tuple(self.v_s.shape) != (p, h, ps) \
+                or tuple(self.k_cp.shape) != (p, h, 2, HEAD_DIM) or tuple(self.v_cp.shape) != (p, h, 2, HEAD_DIM):
+            raise ValueError("per-channel cache tensors do not match the documented layout")
+        for t in (self.k_codes, self.v_codes, self.k_s, self.v_s, self.k_cp, self.v_cp):
+            if not t.is_contiguous():
+                raise ValueError("cache tensors must be contiguous")
+
+
+def pc_write_pages(k: torch.Tensor, v: torch.Tensor, page_ids: torch.Tensor, cache: PagedKVCachePC,
+                   hadamard_block: int, stream=None) -> None:
+    """kvq_pc_write_pages: k, v bf16 [n * ps, H, 128] (contiguous heads), input page i = tokens
+    i * ps .. i * ps + ps - 1, written to cache page page_ids[i] (int32 [n])."""
+    cache._check_layout()
+    ps = cache.page_size
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or t.shape[1] != cache.num_kv_heads or t.shape[2] != HEAD_DIM or t.stride(2) != 1 \
+                or t.stride(1) != HEAD_DIM or t.shape[0] % ps:
+            raise ValueError(f"{name} must be [n * {ps}, {cache.num_kv_heads}, {HEAD_DIM}] with contiguous heads")
+    n = k.shape[0] // ps
+    if v.shape[0] != k.shape[0] or page_ids.shape != (n,) or not page_ids.is_contiguous():
+        raise ValueError("k, v and page_ids disagree on the number of pages")
+    st = lib().kvq_pc_write_pages(
+        _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16), k.stride(0), v.stride(0), n,
+        _dev(page_ids, "page_ids", torch.int32), cache.num_kv_heads, HEAD_DIM,
+        _dev(cache.k_codes, "k_codes", torch.uint8), _dev(cache.v_codes, "v_codes", torch.uint8),
+        _dev(cache.k_s, "k_s", torch.float32), _dev(cache.v_s, "v_s", torch.float32),
+        _dev(cache.k_cp, "k_cp", torch.float32), _dev(cache.v_cp, "v_cp", torch.float32),
+        cache.num_pages, ps, hadamard_block, cache.bits, _stream(stream))
+    _check(st, "kvq_pc_write_pages")
+
+
+def pc_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int, page_size: int,
+                             pages_per_split: int = 0) -> int:
+    return int(lib().kvq_pc_decode_workspace_size(batch, num_q_heads, num_kv_heads, HEAD_DIM, max_context_len,
+                                                  page_size, pages_per_split))
+
+
+def pc_decode_attention(q: torch.Tensor, cache: PagedKVCachePC, block_table: torch.Tensor,
+                        context_lens: torch.Tensor, max_context_len: int, tail_k: torch.Tensor, tail_v: torch.Tensor,
+                        hadamard_block: int, softmax_scale: float = 0.0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, pages_per_split: int = 0, stream=None) -> torch.Tensor:
+    """kvq_pc_decode_attention: q bf16 [B, Hq, 128]; sequence b's context_lens[b] // ps complete pages
+    come from block_table[b], its context_lens[b] % ps newest tokens from tail_k / tail_v
+    (bf16 [B, ps, H, 128]). Returns float32 [B, Hq, 128]."""
+    cache._check_layout()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    bsz, hq, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] int32 tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+    tail_shape = (bsz, cache.page_size, cache.num_kv_heads, HEAD_DIM)
+    for name, t in (("tail_k", tail_k), ("tail_v", tail_v)):
+        if tuple(t.shape) != tail_shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {list(tail_shape)} bf16 tensor")
+    if out is None:
+        out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (bsz, hq, HEAD_DIM) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
+    if workspace is None:
+        workspace = decode_workspace(pc_decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len,
+                                                              cache.page_size, pages_per_split), q.device)
+    st = lib().kvq_pc_decode_attention(
+        _dev(q, "q", torch.bfloat16), _dev(cache.k_codes, "k_codes", torch.uint8),
+        _dev(cache.v_codes, "v_codes", torch.uint8), _dev(cache.k_s, "k_s", torch.float32),
+        _dev(cache.v_s, "v_s", torch.float32), _dev(cache.k_cp, "k_cp", torch.float32),
+        _dev(cache.v_cp, "v_cp", torch.float32), cache.num_pages, cache.page_size,
+        _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len,
+        _dev(tail_k, "tail_k", torch.bfloat16), _dev(tail_v, "tail_v", torch.bfloat16), bsz, hq,
+        cache.num_kv_heads, HEAD_DIM, hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream))
+    _check(st, "kvq_pc_decode_attention")
     return out

@@ -198,3 +198,50 @@ def test_prefill_validation_and_workspace():
     assert L.kvq_paged_prefill_workspace_size(64, 16, 32, 8, 128, 4096, 16, 0) == 0
     w = L.kvq_paged_prefill_workspace_size(1, 4, 32, 8, 128, 4096, 16, 0)
     assert w >= 2 * 4 * 32 * 130 * 4
+
+
+def _pc_write(**kw):
+    a = dict(k=NULL, v=NULL, ks=1024, vs=1024, n=2, ids=NULL, h=8, d=128, kc=NULL, vc=NULL, kss=NULL, vss=NULL,
+             kcp=NULL, vcp=NULL, pages=10, ps=32, hb=128, bits=2)
+    a.update(kw)
+    return kvq.lib().kvq_pc_write_pages(a["k"], a["v"], a["ks"], a["vs"], a["n"], a["ids"], a["h"], a["d"], a["kc"],
+                                        a["vc"], a["kss"], a["vss"], a["kcp"], a["vcp"], a["pages"], a["ps"], a["hb"],
+                                        a["bits"], NULL)
+
+
+def _pc_decode(**kw):
+    a = dict(q=NULL, kc=NULL, vc=NULL, kss=NULL, vss=NULL, kcp=NULL, vcp=NULL, pages=10, ps=64, bt=NULL, mp=8,
+             cl=NULL, mcl=500, tk=NULL, tv=NULL, b=2, hq=32, hkv=8, d=128, hb=128, bits=4, ss=0.0, out=NULL,
+             ws=NULL, wsb=0, pps=0)
+    a.update(kw)
+    return kvq.lib().kvq_pc_decode_attention(
+        a["q"], a["kc"], a["vc"], a["kss"], a["vss"], a["kcp"], a["vcp"], a["pages"], a["ps"], a["bt"], a["mp"],
+        a["cl"], a["mcl"], a["tk"], a["tv"], a["b"], a["hq"], a["hkv"], a["d"], a["hb"], a["bits"], a["ss"], a["out"],
+        a["ws"], a["wsb"], a["pps"], NULL)
+
+
+def test_pc_validation_and_workspace():
+    assert _pc_write(n=0) == kvq.KVQ_OK
+    assert _pc_write() == kvq.KVQ_ERR_NULL
+    assert _pc_write(n=-1) == kvq.KVQ_ERR_SHAPE
+    assert _pc_write(ps=16) == kvq.KVQ_ERR_UNSUPPORTED      # per-channel pages are 32 or 64 tokens
+    assert _pc_write(ps=128) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_write(ps=48) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_write(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_write(hb=3) == kvq.KVQ_ERR_SHAPE
+    assert _pc_write(ks=1000) == kvq.KVQ_ERR_SHAPE          # stride below one token's heads
+    assert _pc_write(ks=1028) == kvq.KVQ_ERR_SHAPE          # stride not a multiple of 8
+    assert _pc_decode(b=0) == kvq.KVQ_OK
+    assert _pc_decode() == kvq.KVQ_ERR_NULL
+    assert _pc_decode(ps=16) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_decode(hq=31) == kvq.KVQ_ERR_SHAPE
+    assert _pc_decode(hq=72) == kvq.KVQ_ERR_UNSUPPORTED     # 9 query heads per KV head
+    assert _pc_decode(mp=6) == kvq.KVQ_ERR_SHAPE            # 500 // 64 = 7 complete pages need 7 entries
+    assert _pc_decode(mp=7, b=0) == kvq.KVQ_OK
+    # workspace: page splits over the complete pages plus the tail split, (splits + 1) rows each
+    ws = kvq.lib().kvq_pc_decode_workspace_size
+    one = ws(1, 4, 1, 128, 63, 64, 0)                       # no complete page: one empty page split + the tail
+    assert one == 2 * 4 * 128 * 4 + 256                     # two splits of 4 rows (acc), then (max, sum) rounded up
+    assert ws(2, 32, 8, 128, 4096, 64, 0) > ws(2, 32, 8, 128, 4096, 64, 64)
+    assert ws(2, 32, 8, 128, 4096, 64, 64) == 2 * 2 * 32 * 128 * 4 + 1024   # 128 rows of (max, sum)
+    assert ws(0, 32, 8, 128, 4096, 64, 0) == 0
