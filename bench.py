@@ -49,8 +49,11 @@ def parse_args():
                    help="print the HBM traffic summary of two rocprofv3 --pmc runs of --counters")
     p.add_argument("--suite", action="store_true",
                    help="time every workload shape (tiny, batch sweep with and without rotation, the 80-layer "
-                        "Llama-2-70B step, the chunked OScaR INT2 prefill) and print one JSON line each")
+                        "Llama-2-70B step, the chunked OScaR INT2 prefill, per-channel pages, several queries per "
+                        "sequence) and print one JSON line each")
     p.add_argument("--suite-cpu", action="store_true", help="with --suite: also time the CPU oracle on small samples")
+    p.add_argument("--suite-only", default="",
+                   help="with --suite: run only these parts (comma list of tiny, sweep, llama2_70b, oscar, pc, multi_query)")
     p.add_argument("--summarize-kernel-stats", metavar="RUN_DIR",
                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run as markdown")
     return p.parse_args()
@@ -484,6 +487,84 @@ def suite_oscar(dev, stream, cpu):
     return [row]
 
 
+def pc_write_bytes(tokens: int, heads: int, bits: int, page_size: int, d: int = 128) -> int:
+    """Algorithmic bytes of kvq_pc_write_pages: bf16 K+V read; codes, a float32 scale per token and
+    a float32 (scale, zero) per channel per page written for K and V; the page ids."""
+    pages = tokens // page_size
+    return tokens * heads * (2 * d * 2 + 2 * d * bits // 8 + 2 * 4) + pages * heads * 2 * 2 * d * 4 + pages * 4
+
+
+def pc_decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size: int, d: int = 128) -> int:
+    """Algorithmic bytes of kvq_pc_decode_attention: codes and token scales of every token in a
+    complete page, each page's K and V (scale, zero) per channel, the bf16 tail tokens, block-table
+    entries, bf16 q, fp32 out, the context lengths."""
+    lens = np.asarray(lens)
+    full = lens // page_size
+    toks = int(np.sum(full)) * page_size
+    tail = int(np.sum(lens - full * page_size))
+    b = len(lens)
+    return (toks * num_kv_heads * (2 * d * bits // 8 + 2 * 4) + int(np.sum(full)) * num_kv_heads * 2 * 2 * d * 4
+            + tail * num_kv_heads * 2 * d * 2 + int(np.sum(full)) * 4 + b * num_q_heads * d * (2 + 4) + b * 4)
+
+
+def suite_pc(dev, stream, cpu):
+    """Per-channel OScaR pages on the OScaR INT2 shape (32 x 16384 tokens, 28/4 heads) with pages of 64
+    and of 128 tokens: the whole prefill written page by page, then a decode step whose newest token
+    sits in the bf16 residual window."""
+    return [_pc_row(dev, stream, ps) for ps in (64, 128)]
+
+
+def _pc_row(dev, stream, ps):
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("oscar_int2")
+    hb, bits = shape.hadamard_block, shape.bits
+    bsz, heads = shape.batch, shape.num_kv_heads
+    per_seq = shape.context_lens[0] // ps
+    n_pages = bsz * per_seq
+    k, v = W.draw_kv_device(shape, n_pages * ps, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(shape.seed + 64)
+    ids = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32)
+    bt = ids.view(bsz, per_seq).contiguous()
+    cache = kvq.PagedKVCachePC.empty(n_pages, heads, ps, bits, device=dev)
+    kvq.pc_write_pages(k, v, ids, cache, hb, stream=stream)
+    torch.cuda.synchronize()
+    t_write = _timed(lambda i: kvq.pc_write_pages(k, v, ids, cache, hb, stream=stream), 5, stream)
+    del k, v
+    copies = [cache] + [kvq.PagedKVCachePC(cache.k_codes.clone(), cache.v_codes.clone(), cache.k_s.clone(),
+                                           cache.v_s.clone(), cache.k_cp.clone(), cache.v_cp.clone(), bits)
+                        for _ in range(7)]
+    tail_k, tail_v = (torch.randn((bsz, ps, heads, 128), generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    lens_np = np.full(bsz, per_seq * ps + 1, dtype=np.int32)   # the prefill plus the new token, in the tail
+    lens = torch.from_numpy(lens_np).to(dev)
+    q = torch.randn((bsz, shape.num_q_heads, 128), generator=g, device=dev).to(torch.bfloat16)
+    max_len = int(lens_np.max())
+    ws = kvq.decode_workspace(kvq.pc_decode_workspace_size(bsz, shape.num_q_heads, heads, max_len, ps), dev)
+    out = torch.empty((bsz, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def attend(i):
+        kvq.pc_decode_attention(q, copies[i % len(copies)], bt, lens, max_len, tail_k, tail_v, hb, out=out,
+                                workspace=ws, stream=stream)
+    for i in range(5):
+        attend(i)
+    t_att = _timed(attend, 50, stream)
+    b_att = pc_decode_bytes(lens_np, shape.num_q_heads, heads, bits, ps)
+    b_write = pc_write_bytes(n_pages * ps, heads, bits, ps)
+    del copies, cache
+    torch_empty_cache()
+    gbps_att = b_att / t_att / 1e6
+    row = _line(workload=f"OScaR per-channel INT2 pages of {ps} tokens, 32 x 16385 tokens, 28/4 heads",
+                batch=bsz, page_size=ps, pages=n_pages,
+                write_ms=round(t_write, 5), write_GBps=round(b_write / t_write / 1e6, 1),
+                write_tokens_per_s=round(n_pages * ps / (t_write * 1e-3), 1),
+                attention_ms=round(t_att, 5), attention_bytes=b_att, attention_GBps=round(gbps_att, 1),
+                attention_frac_of_peak=round(gbps_att / PEAK_HBM_GBPS, 4),
+                cache_bytes_per_token_head=round((2 * 128 * bits // 8 + 8) + 2 * 2 * 128 * 4 / ps, 1))
+    return row
+
+
 def suite_multi_query(dev, stream, cpu):
     """Several queries per sequence over the low-bit cache: speculative verification (4 draft
     tokens per sequence, Llama-3-8B shape) and a 512-token chunk of chunked prefill (OScaR INT2
@@ -578,7 +659,10 @@ def run_suite(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     rows = []
-    for fn in (suite_tiny, suite_sweep, suite_llama2_70b, suite_oscar, suite_multi_query):
+    only = {x for x in args.suite_only.split(",") if x}
+    for fn in (suite_tiny, suite_sweep, suite_llama2_70b, suite_oscar, suite_pc, suite_multi_query):
+        if only and fn.__name__[len("suite_"):] not in only:
+            continue
         new = fn(dev, stream, args.suite_cpu)
         for r in new:
             print(json.dumps(r), flush=True)

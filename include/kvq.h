@@ -281,7 +281,7 @@ kvq_status kvq_paged_decode_attention_bf16(
  *   k_cp, v_cp         float [num_pages][num_kv_heads][2][head_dim]       {scale[head_dim], zero[head_dim]}
  *   tail_k, tail_v     bf16 [batch][page_size][num_kv_heads][head_dim]    sequence b's newest
  *                      context_lens[b] % page_size tokens, oldest first
- * page_size must be 32 or 64 (KVQ_ERR_UNSUPPORTED otherwise). Alignment: k, v, codes, k_cp, v_cp,
+ * page_size must be 32, 64 or 128 (KVQ_ERR_UNSUPPORTED otherwise). Alignment: k, v, codes, k_cp, v_cp,
  * tail_k, tail_v, q, out 16 bytes; k_s, v_s, page_ids, block_table, context_lens 4.
  */
 

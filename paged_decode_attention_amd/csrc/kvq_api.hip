@@ -489,7 +489,7 @@ namespace {
 
 kvq_status check_pc(int32_t head_dim, int32_t page_size, int32_t hadamard_block, int32_t bits) {
   if (kvq_status s = check_common(head_dim, page_size, hadamard_block, bits)) return s;
-  if (page_size != 32 && page_size != kvq::kPcMaxPage) return KVQ_ERR_UNSUPPORTED;
+  if (page_size != 32 && page_size != 64 && page_size != kvq::kPcMaxPage) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 

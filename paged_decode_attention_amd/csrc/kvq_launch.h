@@ -95,7 +95,7 @@ struct DecodeArgs {
 
 // Per-channel pages (the per-channel reading of OScaR): codes as in the token-wise cache, a
 // float32 scale per token, a float32 (scale, zero) per channel per page-head.
-constexpr int kPcMaxPage = 64;    // page sizes 32 and 64
+constexpr int kPcMaxPage = 128;   // page sizes 32, 64 and 128
 
 struct PcWriteArgs {
   const uint16_t* k;

@@ -33,14 +33,14 @@ namespace {
 // ---------------------------------------------------------------------------- write path
 // One workgroup of four waves per (input page, KV head, tensor). Row group r = 4 wave + G takes
 // tokens r, r + 16, ...; its 16 lanes hold the token's 128 channels, 8 each.
-template <int BITS>
+template <int BITS, int MAXPS>
 __global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
   constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
   constexpr int kRow = kHeadDim * BITS / 8;  // code bytes per token
   constexpr int kPer = 8 / BITS;             // codes per byte
-  __shared__ float us[kPcMaxPage][kHeadDim];  // normalised rotated tokens u
+  __shared__ float us[MAXPS][kHeadDim];       // normalised rotated tokens u (page_size <= MAXPS)
   __shared__ float mm[2][2][kHeadDim];        // [min | max][half of the tokens][channel]
-  __shared__ float cps[2][kHeadDim];          // [scale | zero][channel]
+  __shared__ float cps[4][kHeadDim];          // [scale m | zero | 1 / (scale m) | m][channel]
 
   const int32_t page = a.page_ids[blockIdx.x];
   if (page < 0 || page >= a.num_pages) return;  // uniform per workgroup
@@ -56,10 +56,22 @@ __global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
   float* s_out = (is_v ? a.v_s : a.k_s) + tile * ps;
   const LaneFwht lf = lane_fwht(a.rot, n);
 
-  for (int t = (tid >> 6) * 4 + G; t < ps; t += 16) {
-    float x[8];
+  // every load of the row group's tokens is issued before any of them is processed
+  constexpr int kPerRow = MAXPS / 16;
+  const int r0 = (tid >> 6) * 4 + G;
+  uint4 raw[kPerRow];
+#pragma unroll
+  for (int i = 0; i < kPerRow; ++i) {
+    const int t = min(r0 + 16 * i, ps - 1);
     const int64_t tok = static_cast<int64_t>(blockIdx.x) * ps + t;
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + tok * stride + h * kHeadDim + 8 * n), x);
+    raw[i] = *reinterpret_cast<const uint4*>(src + tok * stride + h * kHeadDim + 8 * n);
+  }
+#pragma unroll
+  for (int i = 0; i < kPerRow; ++i) {
+    const int t = r0 + 16 * i;
+    if (t >= ps) break;
+    float x[8];
+    bf16x8_to_f32(raw[i], x);
     fwht_row16_planned(x, a.rot, lf);
     double ss = 0.0;  // RMS in double precision, rounded once to float; 1 for an all-zero token
 #pragma unroll
@@ -67,8 +79,13 @@ __global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
     ss = row16_sum_f64(ss);
     float s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
     if (s == 0.0f) s = 1.0f;
+    // x / s from the reciprocal with one correction step; an extreme s and x are first brought
+    // near 1 by the same power of two (exact), so that the reciprocal stays a normal number
+    const float m2 = (s < 0x1p-100f) ? 0x1p100f : ((s > 0x1p100f) ? 0x1p-100f : 1.0f);
+    const float sm = s * m2;
+    const float rs = 1.0f / sm;  // IEEE division
 #pragma unroll
-    for (int k = 0; k < 8; ++k) us[t][8 * lf.pos + k] = x[k] / s;  // IEEE division
+    for (int k = 0; k < 8; ++k) us[t][8 * lf.pos + k] = div_rn(x[k] * m2, sm, rs);
     if (n == 0) s_out[t] = s;
   }
   __syncthreads();
@@ -87,8 +104,12 @@ __global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
     const float mn = fminf(mm[0][0][tid], mm[0][1][tid]);
     const float mx = fmaxf(mm[1][0][tid], mm[1][1][tid]);
     const float scale = (mx - mn) / kQmax;  // IEEE division
-    cps[0][tid] = scale;
+    // codes divide (u - zero) m by scale m, m a power of two that keeps a tiny scale normal
+    const float m2 = (scale < 0x1p-100f) ? 0x1p100f : 1.0f;
+    cps[0][tid] = scale * m2;
     cps[1][tid] = mn;
+    cps[2][tid] = 1.0f / (scale * m2);  // IEEE division (inf for a constant channel, never used then)
+    cps[3][tid] = m2;
     float* cp = (is_v ? a.v_cp : a.k_cp) + tile * 2 * kHeadDim;
     cp[tid] = scale;
     cp[kHeadDim + tid] = mn;
@@ -97,11 +118,12 @@ __global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
 
   // codes, one 32-bit word per work unit: K - word d of token t's row; V - row byte j of the
   // four tokens 4 tg .. 4 tg + 3 (the interleaved V layout)
+  // (u - zero) / scale from the reciprocal with one correction step (both scaled by m, exact)
   auto code = [&](int t, int c) -> uint32_t {
     const float scale = cps[0][c];
     if (scale == 0.0f) return 0u;
-    const float r = rintf((us[t][c] - cps[1][c]) / scale);  // IEEE division, half to even
-    return static_cast<uint32_t>(fminf(fmaxf(r, 0.0f), kQmax));
+    const float qt = div_rn((us[t][c] - cps[1][c]) * cps[3][c], scale, cps[2][c]);
+    return static_cast<uint32_t>(fminf(fmaxf(rintf(qt), 0.0f), kQmax));  // half to even
   };
   auto row_byte = [&](int t, int j) -> uint32_t {
     uint32_t v = 0;
@@ -185,7 +207,7 @@ __device__ __forceinline__ QueryLimbs page_limbs(const float (&qv)[32]) {
 // n_tail bf16 tokens of the unfinished page (lane t scores token t; lane l then accumulates
 // channels 2l, 2l + 1), in the original basis.
 __device__ __forceinline__ void pc_tail(const PcDecodeArgs& a, int b, int kvh, int g, int n_tail, float (&qs)[8][kHeadDim],
-                        float (&pw)[8][64]) {
+                        float (&pw)[8][kPcMaxPage]) {
   const int lane = threadIdx.x;
   // raw query rows (scaled to log2 units)
 #pragma unroll
@@ -201,20 +223,27 @@ __device__ __forceinline__ void pc_tail(const PcDecodeArgs& a, int b, int kvh, i
   const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * kHeadDim;
   const uint16_t* kt = a.tail_k + static_cast<int64_t>(b) * a.page_size * tok_stride + kvh * kHeadDim;
   const uint16_t* vt = a.tail_v + static_cast<int64_t>(b) * a.page_size * tok_stride + kvh * kHeadDim;
-  float s[8];
+  // lane l scores tokens l and l + 64
+  constexpr int kRounds = kPcMaxPage / 64;
+  float s[kRounds][8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s[c] = 0.f;
-  const bool live = lane < n_tail;
-  if (live) {
-    const uint16_t* kr = kt + lane * tok_stride;
-    for (int j = 0; j < kHeadDim / 8; ++j) {
-      float x[8];
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + 8 * j), x);
+  for (int rd = 0; rd < kRounds; ++rd) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        if (c < g) {
+    for (int c = 0; c < 8; ++c) s[rd][c] = kNegInf;
+    const int t = lane + 64 * rd;
+    if (t < n_tail) {
 #pragma unroll
-          for (int k = 0; k < 8; ++k) s[c] = __builtin_fmaf(qs[c][8 * j + k], x[k], s[c]);
+      for (int c = 0; c < 8; ++c) s[rd][c] = 0.f;
+      const uint16_t* kr = kt + t * tok_stride;
+      for (int j = 0; j < kHeadDim / 8; ++j) {
+        float x[8];
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(kr + 8 * j), x);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c < g) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s[rd][c] = __builtin_fmaf(qs[c][8 * j + k], x[k], s[rd][c]);
+          }
         }
       }
     }
@@ -222,15 +251,20 @@ __device__ __forceinline__ void pc_tail(const PcDecodeArgs& a, int b, int kvh, i
   float m[8], l[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    float v = live ? s[c] : kNegInf;
-    float mx = v;
+    float mx = s[0][c];
+#pragma unroll
+    for (int rd = 1; rd < kRounds; ++rd) mx = fmaxf(mx, s[rd][c]);
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    const float p = (live && mx != kNegInf) ? __builtin_amdgcn_exp2f(v - mx) : 0.f;
-    float sum = p;
+    float sum = 0.f;
+#pragma unroll
+    for (int rd = 0; rd < kRounds; ++rd) {
+      const float p = (s[rd][c] != kNegInf) ? __builtin_amdgcn_exp2f(s[rd][c] - mx) : 0.f;  // no token: 0
+      sum += p;
+      pw[c][lane + 64 * rd] = p;
+    }
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
     m[c] = mx;
     l[c] = sum;
-    pw[c][lane] = p;
   }
   wave_lds_sync();
   float acc[8][2];
@@ -265,7 +299,7 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
   __shared__ float qs[8][kHeadDim];            // rotated query rows (log2 units); raw ones for the tail
   __shared__ float4 szs[2][kNT][16];           // token scales of a step's tiles: [buf][tile][K 0..3 | V 4..7]
   __shared__ float cps[2][4][kHeadDim];        // page parameters: [page parity][K scale, K zero, V scale, V zero]
-  __shared__ float pw[8][64];                  // tail softmax weights
+  __shared__ float pw[8][kPcMaxPage];          // tail softmax weights
 
   const int lane = threadIdx.x;
   const int G = lane >> 4;
@@ -401,25 +435,47 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
     const int par = p & 1;
     float qv[32];
     float zp = 0.f;
+    // the lane's 32 channels are 32G .. 32G + 31: read them four at a time and place each
+    // in the operand slot (j, r, k) whose channel it is
+    const float4* qrow = reinterpret_cast<const float4*>(&qs[n < g ? n : 0][32 * G]);
+    const float4* krow = reinterpret_cast<const float4*>(&cps[par][0][32 * G]);
+    const float4* zrow = reinterpret_cast<const float4*>(&cps[par][1][32 * G]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int f = 0; f < 8; ++f) {
+      const float4 q4 = qrow[f], k4 = krow[f], z4 = zrow[f];
+      const float qq[4] = {q4.x, q4.y, q4.z, q4.w};
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int ch = qk_channel<BITS>(G, j, r, k);
-          const float q = (n < g) ? qs[n][ch] : 0.f;
-          qv[(j * 4 + r) * 4 + k] = q * cps[par][0][ch];
-          zp = __builtin_fmaf(q, cps[par][1][ch], zp);
+      for (int e = 0; e < 4; ++e) {
+        const int off = 4 * f + e;  // channel 32G + off
+        int slot;
+        if constexpr (BITS == 4) {  // off = 16 j + 8 (r >> 1) + 2 k + (r & 1)
+          const int j = off >> 4, rh = (off >> 3) & 1, k = (off >> 1) & 3, rl = off & 1;
+          slot = (j * 4 + 2 * rh + rl) * 4 + k;
+        } else {                    // off = 16 j + 4 k + r
+          const int j = off >> 4, k = (off >> 2) & 3, r = off & 3;
+          slot = (j * 4 + r) * 4 + k;
         }
+        const float q = (n < g) ? qq[e] : 0.f;
+        qv[slot] = q * kk[e];
+        zp = __builtin_fmaf(q, zz[e], zp);
+      }
+      if (f & 1) __builtin_amdgcn_sched_barrier(0);  // bound the reads in flight (registers)
+    }
     zp += __shfl_xor(zp, 16, 64);
     zp += __shfl_xor(zp, 32, 64);
     zq = zp;
     L = page_limbs<BITS>(qv);
+    const float4* vrow = reinterpret_cast<const float4*>(&cps[par][2][8 * n]);
+    const float4* vzrow = reinterpret_cast<const float4*>(&cps[par][3][8 * n]);
+    const float4 d0 = vrow[0], d1 = vrow[1], e0 = vzrow[0], e1 = vzrow[1];
+    const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const float ee[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      dv[m] = cps[par][2][8 * n + m];
-      zv[m] = __builtin_fmaf(-VBias<BITS>::value, dv[m], cps[par][3][8 * n + m]);
+      dv[m] = dd[m];
+      zv[m] = __builtin_fmaf(-VBias<BITS>::value, dd[m], ee[m]);
     }
   };
   auto page_end = [&](int p) {
@@ -574,8 +630,14 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
 
 hipError_t launch_pc_write(const PcWriteArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.num_input_pages), static_cast<unsigned>(a.num_kv_heads), 2);
-  if (a.bits == 4) hipLaunchKernelGGL(pc_write_kernel<4>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(pc_write_kernel<2>, grid, dim3(256), 0, stream, a);
+  // the LDS copy of the page is sized for 64 or 128 tokens (more workgroups per CU for small pages)
+  if (a.page_size <= 64) {
+    if (a.bits == 4) hipLaunchKernelGGL((pc_write_kernel<4, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((pc_write_kernel<2, 64>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (a.bits == 4) hipLaunchKernelGGL((pc_write_kernel<4, kPcMaxPage>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((pc_write_kernel<2, kPcMaxPage>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

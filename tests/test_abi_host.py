@@ -224,8 +224,8 @@ def test_pc_validation_and_workspace():
     assert _pc_write(n=0) == kvq.KVQ_OK
     assert _pc_write() == kvq.KVQ_ERR_NULL
     assert _pc_write(n=-1) == kvq.KVQ_ERR_SHAPE
-    assert _pc_write(ps=16) == kvq.KVQ_ERR_UNSUPPORTED      # per-channel pages are 32 or 64 tokens
-    assert _pc_write(ps=128) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_write(ps=16) == kvq.KVQ_ERR_UNSUPPORTED      # per-channel pages are 32, 64 or 128 tokens
+    assert _pc_write(ps=256) == kvq.KVQ_ERR_UNSUPPORTED
     assert _pc_write(ps=48) == kvq.KVQ_ERR_UNSUPPORTED
     assert _pc_write(bits=3) == kvq.KVQ_ERR_UNSUPPORTED
     assert _pc_write(hb=3) == kvq.KVQ_ERR_SHAPE

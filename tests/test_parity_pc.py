@@ -98,7 +98,7 @@ def _compare_pc_caches(got: O.PagedCachePC, ref: O.PagedCachePC, ids, diag, what
     _say(f"  {what}: {len(ids)} pages, boundary mismatches {n_bad}")
 
 
-@pytest.mark.parametrize("ps", [32, 64])
+@pytest.mark.parametrize("ps", [32, 64, 128])
 @pytest.mark.parametrize("bits,hb", [(2, 128), (4, 128), (4, 32), (2, 1)])
 def test_pc_write(ps, bits, hb):
     shape = W.config("oscar_int2", batch=3, num_q_heads=28, num_kv_heads=4).with_(context_lens=(2 * ps + 5, ps, 3 * ps))
@@ -153,7 +153,7 @@ def _decode_case(name, shape, ps, bits, hb, pps_list, seed, heads=None):
             H.check_attention(got, ref, f"{name} pps {pps}", heads=heads)
 
 
-@pytest.mark.parametrize("ps", [32, 64])
+@pytest.mark.parametrize("ps", [32, 64, 128])
 @pytest.mark.parametrize("bits", [2, 4])
 def test_pc_decode_ragged(ps, bits):
     # empty, tail only, exact pages, pages + tail, one token; g = 7 (28 / 4 heads)
