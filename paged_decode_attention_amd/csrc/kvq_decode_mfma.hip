@@ -220,9 +220,14 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   const int tiles_per_page = PS16 ? 1 : ps / 16;
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + ps - 1) / ps;
-  const int p_begin = split * a.pages_per_split;
-  // the last split also takes the pages past num_splits * pages_per_split (see plan_splits)
-  const int p_end = (split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split);
+  // The pages past num_splits * pages_per_split (see plan_splits) go to the last split, or, in the
+  // fused step, to the first: the split that writes the new token (the last page's) is then not
+  // also the longest one.
+  const int extra = max(0, n_pages - a.num_splits * a.pages_per_split);
+  const bool extra_first = a.fused && extra > 0 && a.num_splits > 1;
+  const int p_begin = split * a.pages_per_split + ((extra_first && split > 0) ? extra : 0);
+  const int p_end = extra_first ? min(n_pages, (split + 1) * a.pages_per_split + extra)
+                                : ((split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split));
   // queries of this sequence (MQ; never more than its tokens) and the tile's valid columns
   const int qlen = MQ ? min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len) : 1;
   const int ncols = MQ ? min(16, qlen * g - c0) : g;
