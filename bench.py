@@ -688,8 +688,8 @@ def main():
         run_suite(args)
         return
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the kernels run on one GPU's share of the work and this build has "
-              "no multi-GPU path (see the sharding paragraph of the design notes); use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the kernels run on one GPU's share of the work (one GPU's KV heads "
+              "or sequences), and the library has no multi-GPU path; use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -37,8 +37,7 @@ constant 1/sqrt(b); the quantizer runs in float32 with IEEE division and round-h
 even; the optional per-token scale is the float32 rounding of an RMS computed in float64;
 attention accumulates in float64 and returns float32.
 
-Readings of points the pages leave open (each is listed with its reason in the design
-notes of the repository):
+Readings of points the pages leave open:
   * Hadamard: Sylvester order, H[i, j] = (-1)^popcount(i & j), normalised by 1/sqrt(b), no
     random signs; blocks are contiguous channel ranges; the same matrix for K, V and Q.
   * Quantizer: scale = (max - min) / (2^bits - 1), zero = min (a float offset),
@@ -58,6 +57,9 @@ notes of the repository):
       K/V sz   [num_pages][kv_heads][page_size][2] float32 = {scale, zero}
     slot = page * page_size + offset; a negative slot skips the token.
   * GQA: query head h reads KV head h // (num_q_heads // num_kv_heads).
+  * Per-channel pages: the page is the group that shares one (scale, zero) per channel; the
+    per-token scale is the same RMS (parity unpinned as to the norm); a page is quantized
+    once complete, and a sequence's newest (length mod page_size) tokens are attended in bf16.
   * Softmax scale 1/sqrt(D) unless given; output float32, in the original (un-rotated)
     basis; a sequence of length 0 yields zeros.
 """
