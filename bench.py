@@ -266,8 +266,37 @@ def _filled_caches(shape, plan, n_copies, dev, stream, layer=0):
     return caches
 
 
+def _timed_graph(fn, n_inner, n_rep):
+    """Average ms of fn(i) when n_inner calls are captured in one HIP graph and the graph is replayed
+    n_rep times: the GPU time of launch-bound calls without the host's per-call launch cost. fn must
+    launch on the current stream (the capture stream while capturing)."""
+    import torch
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_inner):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_rep):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (n_rep * n_inner)
+
+
 def _decode_step_fns(shape, plan, caches, dev, stream, layer=0):
-    """(append, attend) closures for one decode step of ``shape`` on cache copy i."""
+    """(append, attend) closures for one decode step of ``shape`` on cache copy i (stream None: the
+    current stream at call time)."""
     import torch
     from paged_decode_attention_amd import kvq
     from paged_decode_attention_amd import workloads as W
@@ -369,6 +398,14 @@ def suite_sweep(dev, stream, cpu):
                               attention_GBps=round(b_att / t_att / 1e6, 1),
                               step_GBps=round((b_att + b_app) / t_step / 1e6, 1),
                               tokens_per_s=round(b / (t_step * 1e-3), 1)))
+            if b <= 32:
+                # small batches are launch-bound: the same calls replayed from a HIP graph
+                g_append, g_attend, _ = _decode_step_fns(shape, plan, caches, dev, None)
+                t_g_att = _timed_graph(g_attend, 20, 10)
+                t_g_step = _timed_graph(lambda i: (g_append(i), g_attend(i)), 20, 10)
+                rows[-1].update(graph_attention_ms=round(t_g_att, 5), graph_step_ms=round(t_g_step, 5),
+                                graph_attention_GBps=round(b_att / t_g_att / 1e6, 1),
+                                graph_tokens_per_s=round(b / (t_g_step * 1e-3), 1))
             del caches
             if hb == 64:
                 t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream)
@@ -623,8 +660,13 @@ def suite_tiny(dev, stream, cpu):
                    50, stream)
     append, attend, lens = _decode_step_fns(shape, plan, [cache], dev, stream)
     t_step = _timed(lambda i: (append(i), attend(i)), 50, stream)
+    # the same calls replayed from a HIP graph (no host launch cost per call)
+    t_g_pre = _timed_graph(lambda i: kvq.rotate_quantize_append(k, v, slots, cache, shape.hadamard_block, 0), 20, 10)
+    g_append, g_attend, _ = _decode_step_fns(shape, plan, [cache], dev, None)
+    t_g_step = _timed_graph(lambda i: (g_append(i), g_attend(i)), 20, 10)
     return [_line(workload="tiny: 1 x 512 tokens, 8/8 heads, Hadamard block 32 (latency)", prefill_append_ms=round(t_pre, 5),
-                  decode_step_ms=round(t_step, 5))]
+                  decode_step_ms=round(t_step, 5), graph_prefill_append_ms=round(t_g_pre, 5),
+                  graph_decode_step_ms=round(t_g_step, 5))]
 
 
 def _cpu_decode_sample(shape, n_seq):
@@ -795,6 +837,7 @@ def main():
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+
 
     # the same K steps again with an event between every launch: per-launch times inside the step (each event
     # adds a marker packet, a few us per launch)
