@@ -1,9 +1,8 @@
 // C ABI of libkvq: argument validation, workspace sizing and kernel launches. Host code only;
-// every kernel lives in kvq_append.hip, kvq_decode.hip and kvq_dequant.hip.
+// the kernels live in kvq_append.hip, kvq_decode_mfma.hip, kvq_dequant.hip, kvq_baseline_bf16.hip
+// and kvq_pc.hip.
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 
 #include "../../include/kvq.h"
 #include "kvq_launch.h"
@@ -124,7 +123,7 @@ const char* kvq_status_string(int32_t status) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_NULL: return "a required pointer is NULL";
     case KVQ_ERR_SHAPE: return "invalid or inconsistent size, stride, block size or alignment";
-    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (bits must be 2 or 4, head_dim 128, page_size a multiple of 16, at most 8 query heads per KV head)";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (bits must be 2 or 4, head_dim 128, page_size a multiple of 16 (per-channel pages: 32, 64 or 128), at most 8 query heads per KV head for a single query)";
     case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
     case KVQ_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
@@ -255,12 +254,6 @@ kvq_status decode_args(
   a.inv_sqrt_hb = inv_sqrt(hadamard_block);
   a.rot = kvq::make_row_fwht_plan(hadamard_block);
   a.bits = bits;
-  {
-    // KVQ_DECODE_KERNEL=valu selects the VALU kernel (for side-by-side measurements); the
-    // matrix-core kernel is the default.
-    const char* sel = std::getenv("KVQ_DECODE_KERNEL");
-    a.use_valu = (sel && std::strcmp(sel, "valu") == 0) ? 1 : 0;
-  }
   const double scale = softmax_scale > 0.f ? static_cast<double>(softmax_scale) : 1.0 / std::sqrt(static_cast<double>(head_dim));
   a.qk_scale_log2 = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
   a.out = out;
@@ -331,7 +324,6 @@ kvq_status kvq_decode_step(
   a.v_codes_w = v_codes;
   a.k_sz_w = k_sz;
   a.v_sz_w = v_sz;
-  a.use_valu = 0;  // the fused step exists on the matrix-core kernel only
   return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -397,7 +389,6 @@ kvq_status kvq_paged_prefill_attention(
   if (!q_lens) return KVQ_ERR_NULL;
   if (!aligned(q_lens, 4)) return KVQ_ERR_SHAPE;
   a.q_lens = q_lens;
-  a.use_valu = 0;  // the matrix-core kernel only
   return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

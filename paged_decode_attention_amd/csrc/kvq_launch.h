@@ -66,7 +66,6 @@ struct DecodeArgs {
   RowFwhtPlan rot;                // lane plan of the rotation (MFMA kernel)
   int32_t bits;
   float qk_scale_log2;            // softmax_scale * log2(e)
-  int32_t use_valu;               // 1: VALU kernel instead of the MFMA kernel (comparison runs)
   float* out;
   int32_t num_splits;             // splits of the page range per (sequence, kv head)
   int32_t pages_per_split;
