@@ -85,7 +85,8 @@ def decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size
 
 CSRC = os.path.join(ROOT, "paged_decode_attention_amd", "csrc")
 KERNEL_SOURCES = {
-    "append_kernel": ["kvq_append.hip", "kvq_device.h", "kvq_launch.h", "../build.py"],
+    "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h",
+                      "../build.py"],
     "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h",
                            "../build.py"],
     "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "../build.py"],

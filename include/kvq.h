@@ -289,7 +289,8 @@ kvq_status kvq_paged_decode_attention_bf16(
  * k and v (bf16 [num_input_pages * page_size][num_kv_heads][head_dim], token strides as for
  * kvq_rotate_quantize_append) and is written to cache page page_ids[i] (int32 [num_input_pages]);
  * ids outside [0, num_pages) are skipped, and two inputs with the same id race. Writes the codes,
- * s and (scale, zero) of every KV head of those pages. num_input_pages == 0 is a no-op. */
+ * s and (scale, zero) of every KV head of those pages. num_input_pages == 0 is a no-op;
+ * num_input_pages * num_kv_heads * page_size >= 2^30 gives KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_pc_write_pages(
     const uint16_t* k, const uint16_t* v, int64_t k_token_stride, int64_t v_token_stride,
     int32_t num_input_pages, const int32_t* page_ids, int32_t num_kv_heads, int32_t head_dim,

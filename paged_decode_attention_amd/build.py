@@ -26,7 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_dequant.hip",
-           "kvq_baseline_bf16.hip", "kvq_pc.hip"]
+           "kvq_baseline_bf16.hip", "kvq_pc.hip", "kvq_pc_write.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
@@ -42,7 +42,7 @@ CFLAGS = [
 # Per-source extras. The write path never sees a NaN it must order (its min / max run on finite
 # rotated values), so NaN-honouring min / max lowering - a canonicalising move that keeps the DPP
 # row reductions from fusing into single instructions - is switched off there.
-EXTRA_CFLAGS = {"kvq_append.hip": ["-fno-honor-nans"]}
+EXTRA_CFLAGS = {"kvq_append.hip": ["-fno-honor-nans"], "kvq_pc_write.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

@@ -1,6 +1,6 @@
 // C ABI of libkvq: argument validation, workspace sizing and kernel launches. Host code only;
-// the kernels live in kvq_append.hip, kvq_decode_mfma.hip, kvq_dequant.hip, kvq_baseline_bf16.hip
-// and kvq_pc.hip.
+// the kernels live in kvq_append.hip, kvq_decode_mfma.hip, kvq_dequant.hip, kvq_baseline_bf16.hip,
+// kvq_pc_write.hip and kvq_pc.hip.
 #include <cmath>
 #include <cstdint>
 
@@ -502,7 +502,9 @@ kvq_status kvq_pc_write_pages(
     int32_t num_pages, int32_t page_size, int32_t hadamard_block, int32_t bits, hipStream_t stream) {
   if (num_input_pages < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
   if (kvq_status s = check_pc(head_dim, page_size, hadamard_block, bits)) return s;
-  if (num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+  // one workgroup of 4 page_size threads per (input page, KV head), in one grid dimension
+  if (static_cast<int64_t>(num_input_pages) * num_kv_heads * 4 * page_size >= (int64_t{1} << 32))
+    return KVQ_ERR_UNSUPPORTED;
   const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (k_token_stride < row_elems || v_token_stride < row_elems || k_token_stride % 8 || v_token_stride % 8)
     return KVQ_ERR_SHAPE;

@@ -32,6 +32,13 @@ __device__ __forceinline__ float max_over_rows(float v) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+__device__ __forceinline__ float min_over_rows(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fminf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // Orders this wave's LDS writes before its later LDS reads (one-wave workgroups: no s_barrier,
 // and no wait on the global loads in flight).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -1,14 +1,8 @@
-// Per-channel pages: the per-channel reading of OScaR (OScaR abstract on the openalex page: the
-// rotation and the per-token scaling let the per-channel quantization paradigm hold up under
-// extreme compression; zhichai.net summary, "Root Cause: Token Norm Imbalance" and "The OScaR
-// Framework": V-hat = Quant(S (R V))).
-//
-// Write path (pc_write_kernel): a whole page at a time. Each token of the page is rotated
-// (y = R x), divided by its RMS s (u = y / s, so every token has unit RMS), and the page's ps
-// normalised tokens share one asymmetric (scale, zero) per channel:
-//   scale_c = (max_t u_tc - min_t u_tc) / qmax,  zero_c = min_t u_tc,
-//   code_tc = clamp(rint((u_tc - zero_c) / scale_c), 0, qmax).
-// Stored: codes (in the token-wise cache's layout), s per token, (scale, zero) per channel.
+// Per-channel pages, read path: the per-channel reading of OScaR (OScaR abstract on the openalex
+// page: the rotation and the per-token scaling let the per-channel quantization paradigm hold up
+// under extreme compression; zhichai.net summary, "Root Cause: Token Norm Imbalance" and "The
+// OScaR Framework": V-hat = Quant(S (R V))). The pages are written by kvq_pc_write.hip: codes in
+// the token-wise cache's layout, s per token, (scale, zero) per channel of the page's u = y / s.
 //
 // Read path (pc_decode_kernel): k^_t = s_t (scale (.) c_t + zero) in the rotated basis, so
 //   q~ . k^_t = s_t (sum_c (q~_c scale_c) c_tc + sum_c q~_c zero_c):
@@ -29,125 +23,6 @@
 
 namespace kvq {
 namespace {
-
-// ---------------------------------------------------------------------------- write path
-// One workgroup of four waves per (input page, KV head, tensor). Row group r = 4 wave + G takes
-// tokens r, r + 16, ...; its 16 lanes hold the token's 128 channels, 8 each.
-template <int BITS, int MAXPS>
-__global__ __launch_bounds__(256) void pc_write_kernel(const PcWriteArgs a) {
-  constexpr float kQmax = static_cast<float>((1 << BITS) - 1);
-  constexpr int kRow = kHeadDim * BITS / 8;  // code bytes per token
-  constexpr int kPer = 8 / BITS;             // codes per byte
-  __shared__ float us[MAXPS][kHeadDim];       // normalised rotated tokens u (page_size <= MAXPS)
-  __shared__ float mm[2][2][kHeadDim];        // [min | max][half of the tokens][channel]
-  __shared__ float cps[4][kHeadDim];          // [scale m | zero | 1 / (scale m) | m][channel]
-
-  const int32_t page = a.page_ids[blockIdx.x];
-  if (page < 0 || page >= a.num_pages) return;  // uniform per workgroup
-  const int h = blockIdx.y;
-  const bool is_v = blockIdx.z != 0;
-  const int ps = a.page_size;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int G = lane >> 4, n = lane & 15;
-  const uint16_t* src = is_v ? a.v : a.k;
-  const int64_t stride = is_v ? a.v_stride : a.k_stride;
-  const int64_t tile = static_cast<int64_t>(page) * a.num_kv_heads + h;  // (page, head)
-  float* s_out = (is_v ? a.v_s : a.k_s) + tile * ps;
-  const LaneFwht lf = lane_fwht(a.rot, n);
-
-  // every load of the row group's tokens is issued before any of them is processed
-  constexpr int kPerRow = MAXPS / 16;
-  const int r0 = (tid >> 6) * 4 + G;
-  uint4 raw[kPerRow];
-#pragma unroll
-  for (int i = 0; i < kPerRow; ++i) {
-    const int t = min(r0 + 16 * i, ps - 1);
-    const int64_t tok = static_cast<int64_t>(blockIdx.x) * ps + t;
-    raw[i] = *reinterpret_cast<const uint4*>(src + tok * stride + h * kHeadDim + 8 * n);
-  }
-#pragma unroll
-  for (int i = 0; i < kPerRow; ++i) {
-    const int t = r0 + 16 * i;
-    if (t >= ps) break;
-    float x[8];
-    bf16x8_to_f32(raw[i], x);
-    fwht_row16_planned(x, a.rot, lf);
-    double ss = 0.0;  // RMS in double precision, rounded once to float; 1 for an all-zero token
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ss += static_cast<double>(x[k]) * static_cast<double>(x[k]);
-    ss = row16_sum_f64(ss);
-    float s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
-    if (s == 0.0f) s = 1.0f;
-    // x / s from the reciprocal with one correction step; an extreme s and x are first brought
-    // near 1 by the same power of two (exact), so that the reciprocal stays a normal number
-    const float m2 = (s < 0x1p-100f) ? 0x1p100f : ((s > 0x1p100f) ? 0x1p-100f : 1.0f);
-    const float sm = s * m2;
-    const float rs = 1.0f / sm;  // IEEE division
-#pragma unroll
-    for (int k = 0; k < 8; ++k) us[t][8 * lf.pos + k] = div_rn(x[k] * m2, sm, rs);
-    if (n == 0) s_out[t] = s;
-  }
-  __syncthreads();
-  {
-    const int c = tid & (kHeadDim - 1), half = tid >> 7;
-    float mn = __builtin_inff(), mx = -__builtin_inff();
-    for (int t = half; t < ps; t += 2) {
-      mn = fminf(mn, us[t][c]);
-      mx = fmaxf(mx, us[t][c]);
-    }
-    mm[0][half][c] = mn;
-    mm[1][half][c] = mx;
-  }
-  __syncthreads();
-  if (tid < kHeadDim) {
-    const float mn = fminf(mm[0][0][tid], mm[0][1][tid]);
-    const float mx = fmaxf(mm[1][0][tid], mm[1][1][tid]);
-    const float scale = (mx - mn) / kQmax;  // IEEE division
-    // codes divide (u - zero) m by scale m, m a power of two that keeps a tiny scale normal
-    const float m2 = (scale < 0x1p-100f) ? 0x1p100f : 1.0f;
-    cps[0][tid] = scale * m2;
-    cps[1][tid] = mn;
-    cps[2][tid] = 1.0f / (scale * m2);  // IEEE division (inf for a constant channel, never used then)
-    cps[3][tid] = m2;
-    float* cp = (is_v ? a.v_cp : a.k_cp) + tile * 2 * kHeadDim;
-    cp[tid] = scale;
-    cp[kHeadDim + tid] = mn;
-  }
-  __syncthreads();
-
-  // codes, one 32-bit word per work unit: K - word d of token t's row; V - row byte j of the
-  // four tokens 4 tg .. 4 tg + 3 (the interleaved V layout)
-  // (u - zero) / scale from the reciprocal with one correction step (both scaled by m, exact)
-  auto code = [&](int t, int c) -> uint32_t {
-    const float scale = cps[0][c];
-    if (scale == 0.0f) return 0u;
-    const float qt = div_rn((us[t][c] - cps[1][c]) * cps[3][c], scale, cps[2][c]);
-    return static_cast<uint32_t>(fminf(fmaxf(rintf(qt), 0.0f), kQmax));  // half to even
-  };
-  auto row_byte = [&](int t, int j) -> uint32_t {
-    uint32_t v = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) v |= code(t, kPer * j + k) << (BITS * k);
-    return v;
-  };
-  uint8_t* base = (is_v ? a.v_codes : a.k_codes) + tile * ps * kRow;
-  const int units = ps * kRow / 4;
-  for (int u = tid; u < units; u += 256) {
-    uint32_t w = 0;
-    if (!is_v) {
-      const int t = u / (kRow / 4), d = u % (kRow / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w |= row_byte(t, 4 * d + i) << (8 * i);
-      *reinterpret_cast<uint32_t*>(base + t * kRow + 4 * d) = w;
-    } else {
-      const int tg = u / kRow, j = u % kRow;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w |= row_byte(4 * tg + i, j) << (8 * i);
-      *reinterpret_cast<uint32_t*>(base + (tg * kRow + j) * 4) = w;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------- read path
 constexpr int kNT = 2;  // 16-token tiles per step (a page holds a whole number of steps)
@@ -627,19 +502,6 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
 }
 
 }  // namespace
-
-hipError_t launch_pc_write(const PcWriteArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(a.num_input_pages), static_cast<unsigned>(a.num_kv_heads), 2);
-  // the LDS copy of the page is sized for 64 or 128 tokens (more workgroups per CU for small pages)
-  if (a.page_size <= 64) {
-    if (a.bits == 4) hipLaunchKernelGGL((pc_write_kernel<4, 64>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((pc_write_kernel<2, 64>), grid, dim3(256), 0, stream, a);
-  } else {
-    if (a.bits == 4) hipLaunchKernelGGL((pc_write_kernel<4, kPcMaxPage>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((pc_write_kernel<2, kPcMaxPage>), grid, dim3(256), 0, stream, a);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_pc_decode(const PcDecodeArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.num_splits + 1), static_cast<unsigned>(a.num_kv_heads),

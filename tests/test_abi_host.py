@@ -231,6 +231,9 @@ def test_pc_validation_and_workspace():
     assert _pc_write(hb=3) == kvq.KVQ_ERR_SHAPE
     assert _pc_write(ks=1000) == kvq.KVQ_ERR_SHAPE          # stride below one token's heads
     assert _pc_write(ks=1028) == kvq.KVQ_ERR_SHAPE          # stride not a multiple of 8
+    # one grid dimension of 4 page_size threads per (page, head): 2^22 pages x 8 heads x 32 = 2^30
+    assert _pc_write(n=1 << 22) == kvq.KVQ_ERR_UNSUPPORTED
+    assert _pc_write(n=(1 << 22) - 1) == kvq.KVQ_ERR_NULL
     assert _pc_decode(b=0) == kvq.KVQ_OK
     assert _pc_decode() == kvq.KVQ_ERR_NULL
     assert _pc_decode(ps=16) == kvq.KVQ_ERR_UNSUPPORTED

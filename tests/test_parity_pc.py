@@ -130,6 +130,62 @@ def test_pc_write_skips_out_of_range_pages_and_strided_input():
     _compare_pc_caches(_download(dev), ref, ids[keep], {t: diag[t][keep] for t in diag}, "skip/stride")
 
 
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 values that bf16 holds exactly -> bf16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def _degenerate_pages(ps, heads, seed):
+    """Five input pages of small integers times a power of two: (0) every token the same vector,
+    so every channel is constant; (1) two all-zero tokens; (2) magnitudes near 2^-120, so the token
+    RMS is below 2^-100; (3) magnitudes near 2^100, RMS above 2^100; (4) every token a permutation of
+    one multiset of values, channels 0-15 set to one value, so all tokens share one RMS and (for
+    block size 1) sixteen channels are constant."""
+    rng = np.random.default_rng(seed)
+    pages = []
+    ints = lambda *shape: rng.integers(-8, 9, size=shape).astype(np.float32)  # noqa: E731
+    base = ints(1, heads, 128)
+    pages.append(np.repeat(base, ps, axis=0))
+    p1 = ints(ps, heads, 128)
+    p1[3] = 0.0
+    p1[ps - 1] = 0.0
+    pages.append(p1)
+    pages.append(ints(ps, heads, 128) * np.float32(2.0 ** -120))
+    pages.append(ints(ps, heads, 128) * np.float32(2.0 ** 100))
+    vals = ints(heads, 128)
+    vals[:, :16] = 3.0
+    p4 = np.empty((ps, heads, 128), np.float32)
+    for t in range(ps):
+        for h in range(heads):
+            p4[t, h, :16] = 3.0
+            p4[t, h, 16:] = rng.permutation(vals[h, 16:])
+    pages.append(p4)
+    return _bf16_bits(np.concatenate(pages))
+
+
+@pytest.mark.parametrize("bits,hb", [(4, 1), (2, 1), (4, 128), (2, 32)])
+def test_pc_write_degenerate_pages(bits, hb):
+    ps, heads = 32, 2
+    _say(f"pc write degenerate pages: page {ps}, INT{bits}, Hadamard block {hb}")
+    pk = _degenerate_pages(ps, heads, seed=11)
+    pv = _degenerate_pages(ps, heads, seed=12)
+    ids = np.array([4, 0, 6, 2, 5], dtype=np.int32)
+    ref = O.PagedCachePC(7, heads, ps, 128, bits)
+    diag = O.write_pages_pc(ref, pk, pv, ids, hb)
+    dev = _poisoned(7, heads, ps, bits)
+    kvq.pc_write_pages(H.to_dev_bf16(pk), H.to_dev_bf16(pv), H.to_dev(ids), dev, hb)
+    torch.cuda.synchronize()
+    got = _download(dev)
+    _compare_pc_caches(got, ref, ids, diag, f"degenerate INT{bits} b{hb}")
+    # the constant page: zero codes, zero scales, the channel value as zero point
+    for tensor in ("k", "v"):
+        gc, _, gcp = got.read_page(int(ids[0]), 0, tensor)
+        assert np.all(gc == 0) and np.all(gcp[0] == 0), f"{tensor}: constant page gives nonzero codes or scales"
+
+
 def _decode_case(name, shape, ps, bits, hb, pps_list, seed, heads=None):
     c = _case(shape, ps, bits, hb, seed=seed)
     q = W.draw_q(shape)
