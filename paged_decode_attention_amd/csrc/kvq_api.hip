@@ -192,7 +192,7 @@ size_t kvq_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kvq::kHeadDim || page_size <= 0 ||
       max_context_len < 0 || pages_per_split < 0)
     return 0;
-  const kvq::SplitPlan p = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const kvq::SplitPlan p = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
   return workspace_layout(p.num_splits, batch, num_q_heads).total;
 }
 
@@ -229,7 +229,8 @@ kvq_status decode_args(
       !aligned(v_sz, 8) || !aligned(block_table, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_SHAPE;
 
-  const kvq::SplitPlan plan = kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const kvq::SplitPlan plan =
+      kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, q_len_max == 0);
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads, q_len_max > 0 ? q_len_max : 1);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
 
@@ -363,7 +364,8 @@ size_t kvq_paged_prefill_workspace_size(int32_t batch, int32_t max_q_len, int32_
       head_dim != kvq::kHeadDim || page_size <= 0 || max_context_len < 0 || pages_per_split < 0)
     return 0;
   const int32_t tiles = kvq::mq_column_tiles(max_q_len, num_q_heads / num_kv_heads);
-  const kvq::SplitPlan p = kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const kvq::SplitPlan p =
+      kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, false);
   return workspace_layout(p.num_splits, batch, num_q_heads, max_q_len).total;
 }
 
@@ -446,7 +448,7 @@ kvq_status kvq_paged_decode_attention_bf16(
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_SHAPE;
-  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
   kvq::DecodeBf16Args a{};
@@ -488,7 +490,7 @@ kvq_status check_pc(int32_t head_dim, int32_t page_size, int32_t hadamard_block,
 kvq::SplitPlan pc_plan(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,
                        int32_t pages_per_split) {
   const int32_t full_tokens = max_context_len / page_size * page_size;
-  return kvq::plan_splits(batch, num_kv_heads, full_tokens, page_size, pages_per_split);
+  return kvq::plan_splits(batch, num_kv_heads, full_tokens, page_size, pages_per_split, true);
 }
 
 }  // namespace

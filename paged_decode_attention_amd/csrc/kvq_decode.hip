@@ -7,8 +7,10 @@
 
 namespace kvq {
 
+constexpr int64_t kMaxPagesFewSplits = 48;
+
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,
-                      int32_t pages_per_split_request) {
+                      int32_t pages_per_split_request, bool one_query) {
   const int64_t max_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   SplitPlan p{1, static_cast<int32_t>(max_pages > 0 ? max_pages : 1)};
   if (max_pages <= 0) return p;
@@ -26,7 +28,11 @@ SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_l
     // the last full split go to that split when they are at most half a split (e.g. the page
     // of the newest token); only a larger remainder gets a split of its own.
     pps = std::max<int64_t>(1, max_pages / splits);
-    if (splits > 1 && pps > 8) pps &= ~int64_t{1};
+    // With few splits per sequence (a large batch fills the waves by itself), the longest
+    // sequences' waves set the tail when lengths differ; 48 pages (768 tokens of 16) per split
+    // bounds a wave's walk at one more partial per 48 pages.
+    if (one_query && splits <= 8 && pps > kMaxPagesFewSplits) pps = kMaxPagesFewSplits;
+    if (pps < max_pages && pps > 8) pps &= ~int64_t{1};
     const int64_t full = max_pages / pps, rem = max_pages % pps;
     p.pages_per_split = static_cast<int32_t>(pps);
     p.num_splits = static_cast<int32_t>(std::max<int64_t>(1, full + (2 * rem > pps ? 1 : 0)));

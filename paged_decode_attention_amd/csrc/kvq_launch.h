@@ -204,12 +204,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
 
-// Split plan used by both the workspace query and the launch.
+// Split plan used by both the workspace query and the launch. one_query: one query per sequence
+// (decode), where a split of a large batch is capped in length; several queries per sequence
+// fill the waves with column tiles, and their partials grow with the queries, so no cap there.
 struct SplitPlan {
   int32_t num_splits;
   int32_t pages_per_split;
 };
 SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,
-                      int32_t pages_per_split_request);
+                      int32_t pages_per_split_request, bool one_query);
 
 }  // namespace kvq

@@ -92,8 +92,8 @@ def test_decode_validation():
 
 def test_workspace_size():
     L = kvq.lib()
-    # unsplit: no workspace
-    assert L.kvq_paged_decode_workspace_size(256, 32, 8, 128, 8192, 16, 0) == 0
+    # unsplit: no workspace (a batch that fills the waves by itself, sequences of at most 48 pages)
+    assert L.kvq_paged_decode_workspace_size(256, 32, 8, 128, 768, 16, 0) == 0
     w = L.kvq_paged_decode_workspace_size(1, 32, 8, 128, 8192, 16, 0)
     assert w > 0
     # forced split size: splits = ceil(512 / 64) = 8 -> 8 * 32 * 130 floats at least
@@ -119,8 +119,14 @@ def test_split_plan():
     assert _splits(16, 32, 8, (16 * 16 + 9) * 16) == 17
     # Llama-2-70B, 32769 tokens (2049 pages), 4 x 8 items: 64 splits of 32 pages
     assert _splits(4, 64, 8, 32769) == 64
-    # enough (sequence, KV head) items to fill the GPU: no split
-    assert _splits(256, 32, 8, 8193) == 1
+    # enough (sequence, KV head) items to fill the GPU: no split while a sequence fits in 48 pages,
+    # else splits of at most 48 pages (513 pages: 10 of 48, the remaining 33 more than half of one)
+    assert _splits(256, 32, 8, 768) == 1
+    assert _splits(256, 32, 8, 8193) == 11
+    # 32 sequences x 8 heads: the 8 splits of 64 pages that fill the waves become 48-page splits
+    assert _splits(32, 32, 8, 8193) == 11
+    # 16 x 8 items with 1025 pages: 16 splits of 64 pages (more than 8 per sequence: no cap)
+    assert _splits(16, 28, 4, 16385) == 32 and _splits(32, 28, 4, 16385) == 16
     # a forced split size is taken literally
     assert _splits(1, 32, 8, 4097, pps=16) == 17
     assert _splits(1, 32, 8, 4097, pps=1) == 257
