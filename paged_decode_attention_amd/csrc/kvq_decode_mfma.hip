@@ -695,51 +695,71 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
-  const int64_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
+  const uint32_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
   const int q_len_max = a.q_lens ? a.q_len_max : 1;
-  const int b = static_cast<int>(pair / (static_cast<int64_t>(q_len_max) * a.num_q_heads));
+  const int64_t pairs = static_cast<int64_t>(a.batch) * q_len_max * a.num_q_heads;
+  const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
+  // One batch of 32 splits: row group G loads splits s0 + G + 4j (past s_last: s_last again).
+  struct Batch {
+    float2 ml[8];
+    float4 xa[8], xb[8];
+  };
+  auto load_batch = [&](int s0, int s_last, Batch& bt) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sp = min(s0 + G + 4 * j, s_last);
+      const int64_t row = sp * pairs + pair;
+      bt.ml[j] = ml_all[row];
+      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + row * kHeadDim + 8 * n);
+      bt.xa[j] = src[0];
+      bt.xb[j] = src[1];
+    }
+  };
+  // The first batch is loaded before the sequence length (and so the number of splits it uses)
+  // is known: the workspace holds num_splits rows, and the rows this call did not write (stale,
+  // possibly NaN) are dropped by selection below, never multiplied by a zero weight.
+  Batch bt;
+  load_batch(0, a.num_splits - 1, bt);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int b = static_cast<int>(pair / static_cast<uint32_t>(q_len_max * a.num_q_heads));
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + a.page_size - 1) / a.page_size;
   int nu = a.all_splits ? a.num_splits : min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
   if (a.q_lens) {  // a query row past the sequence's queries has no partials: zero output
-    const int j = static_cast<int>((pair / a.num_q_heads) % q_len_max);
+    const int j = static_cast<int>((pair / static_cast<uint32_t>(a.num_q_heads)) % static_cast<uint32_t>(q_len_max));
     if (j >= min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len)) nu = 0;
   }
   const LaneFwht lf = lane_fwht(a.rot, n);
-  const int64_t pairs = static_cast<int64_t>(a.batch) * q_len_max * a.num_q_heads;
-  const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
   float mo = kNegInf, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nu; s0 += 32) {
-    float2 ml[8];
-    float4 xa[8], xb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int sp = min(s0 + G + 4 * j, nu - 1);  // past the end: re-read the last split, weight 0
-      const int64_t row = sp * pairs + pair;
-      ml[j] = ml_all[row];
-      const float4* src = reinterpret_cast<const float4*>(a.ws_acc + row * kHeadDim + 8 * n);
-      xa[j] = src[0];
-      xb[j] = src[1];
-    }
+  for (int s0 = 0;;) {
+    bool use[8];
     float mc = mo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mc = fmaxf(mc, (s0 + G + 4 * j < nu) ? ml[j].x : kNegInf);
+    for (int j = 0; j < 8; ++j) {
+      // a split with no token for this row (several queries: past a query's causal limit) has
+      // maximum -inf and weighs nothing (even when every split so far is such a split)
+      use[j] = s0 + G + 4 * j < nu && bt.ml[j].x != kNegInf;
+      mc = use[j] ? fmaxf(mc, bt.ml[j].x) : mc;
+    }
     const float r = (mo == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mo - mc);
     lsum *= r;
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] *= r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      // a split with no token for this row (several queries: past a query's causal limit) has
-      // maximum -inf and weighs nothing (even when every split so far is such a split)
-      const float f = (s0 + G + 4 * j < nu && ml[j].x != kNegInf) ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
-      lsum = __builtin_fmaf(ml[j].y, f, lsum);
-      o[0] = __builtin_fmaf(xa[j].x, f, o[0]); o[1] = __builtin_fmaf(xa[j].y, f, o[1]);
-      o[2] = __builtin_fmaf(xa[j].z, f, o[2]); o[3] = __builtin_fmaf(xa[j].w, f, o[3]);
-      o[4] = __builtin_fmaf(xb[j].x, f, o[4]); o[5] = __builtin_fmaf(xb[j].y, f, o[5]);
-      o[6] = __builtin_fmaf(xb[j].z, f, o[6]); o[7] = __builtin_fmaf(xb[j].w, f, o[7]);
+      if (!use[j]) continue;
+      const float f = __builtin_amdgcn_exp2f(bt.ml[j].x - mc);
+      lsum = __builtin_fmaf(bt.ml[j].y, f, lsum);
+      o[0] = __builtin_fmaf(bt.xa[j].x, f, o[0]); o[1] = __builtin_fmaf(bt.xa[j].y, f, o[1]);
+      o[2] = __builtin_fmaf(bt.xa[j].z, f, o[2]); o[3] = __builtin_fmaf(bt.xa[j].w, f, o[3]);
+      o[4] = __builtin_fmaf(bt.xb[j].x, f, o[4]); o[5] = __builtin_fmaf(bt.xb[j].y, f, o[5]);
+      o[6] = __builtin_fmaf(bt.xb[j].z, f, o[6]); o[7] = __builtin_fmaf(bt.xb[j].w, f, o[7]);
     }
     mo = mc;
+    s0 += 32;
+    if (s0 >= nu) break;
+    load_batch(s0, nu - 1, bt);
   }
   lse_combine(mo, lsum, o, 16);
   lse_combine(mo, lsum, o, 32);
