@@ -54,6 +54,8 @@ def parse_args():
     p.add_argument("--suite-cpu", action="store_true", help="with --suite: also time the CPU oracle on small samples")
     p.add_argument("--suite-only", default="",
                    help="with --suite: run only these parts (comma list of tiny, sweep, llama2_70b, oscar, pc, multi_query)")
+    p.add_argument("--summarize-sq", nargs=2, metavar=("INST_DIR", "CYCLE_DIR"),
+                   help="print the SQ instruction-mix and wave-state summary of two rocprofv3 --pmc runs")
     p.add_argument("--summarize-kernel-stats", metavar="RUN_DIR",
                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run as markdown")
     return p.parse_args()
@@ -177,6 +179,51 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
             f"FETCH_SIZE x {factors['FETCH_SIZE']:.4f} and writes WRITE_SIZE x {factors['WRITE_SIZE']:.4f} of its true "
             "size; every kernel's counters are scaled by these factors (median over dispatches).", ""]
     return "\n".join(head + lines + ["", TRAFFIC_TAG + json.dumps(rec, sort_keys=True), ""])
+
+
+SQ_INSTS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_VMEM_RD")
+SQ_CYCLES = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA",
+             "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM")
+
+
+def summarize_sq(inst_dir: str, cycle_dir: str, workload: str) -> str:
+    """Instruction mix per wave and the split of wave-cycles between issuing and waiting, from two
+    rocprofv3 --pmc runs of bench.py --counters (median over the dispatches of each kernel and grid)."""
+    def per_dispatch(run_dir, counters):
+        vals = {}
+        for c in counters:
+            seen = {}
+            for k, g, v in _counter_rows(run_dir, c):
+                seen.setdefault((k, g), []).append(v)
+            for key, vs in seen.items():
+                vals.setdefault(key, {})[c] = vs
+        return vals
+    inst = per_dispatch(inst_dir, SQ_INSTS + ("SQ_WAVE_CYCLES",))
+    cyc = per_dispatch(cycle_dir, SQ_CYCLES + ("SQ_WAVE_CYCLES",))
+    med = lambda xs: float(np.median(xs))  # noqa: E731
+    lines = ["| kernel | grid | waves | VALU / wave | SALU / wave | MFMA / wave | VMEM reads / wave |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, g), c in sorted(inst.items()):
+        if k not in KERNEL_SOURCES:
+            continue
+        w = med(c["SQ_WAVES"])
+        lines.append(f"| {k} | {g} | {w:.0f} | {med(c['SQ_INSTS_VALU']) / w:.0f} | {med(c['SQ_INSTS_SALU']) / w:.0f} | "
+                     f"{med(c['SQ_INSTS_MFMA']) / w:.0f} | {med(c['SQ_INSTS_VMEM_RD']) / w:.1f} |")
+    lines += ["", "Share of wave-cycles (SQ_WAVE_CYCLES) per state:", "",
+              "| kernel | grid | " + " | ".join(x[3:].lower() for x in SQ_CYCLES) + " |",
+              "|---|---|" + "---|" * len(SQ_CYCLES)]
+    for (k, g), c in sorted(cyc.items()):
+        if k not in KERNEL_SOURCES:
+            continue
+        wc = med(c["SQ_WAVE_CYCLES"])
+        lines.append(f"| {k} | {g} | " + " | ".join(f"{med(c[x]) / wc:.3f}" for x in SQ_CYCLES) + " |")
+    cmd = ("rocprofv3 --pmc {counters} --output-format csv -d DIR -o run -- python3 bench.py --counters "
+           f"--workload {workload} --steps 3 --warmup 0")
+    head = [f"# Instruction mix and wave states, {workload}", "",
+            "Commands (two runs, one per counter set; at most 8 SQ counters per run):", "",
+            "- `" + cmd.format(counters=" ".join(SQ_INSTS + ("SQ_WAVE_CYCLES",))) + "`",
+            "- `" + cmd.format(counters=" ".join(("SQ_WAVE_CYCLES",) + SQ_CYCLES)) + "`", ""]
+    return "\n".join(head + lines + [""])
 
 
 def _clean_kernel_name(name: str) -> str:
@@ -721,6 +768,9 @@ def main():
         cmd = (f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d DIR -o run -- python3 bench.py "
                f"--counters --workload {args.workload} --steps {args.steps} --warmup 0")
         print(summarize_counters(*args.summarize_counters, args.workload, cmd))
+        return
+    if args.summarize_sq:
+        print(summarize_sq(*args.summarize_sq, args.workload))
         return
     if args.summarize_kernel_stats:
         cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
