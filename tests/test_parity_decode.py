@@ -158,17 +158,21 @@ def test_dequant_page(tensor, bits, ts, hb):
 
 # ----------------------------------------------------------------------------- full sizes
 
-def _full_size_sampled(name, n_samples, layer=0):
+def _full_size_sampled(name, n_samples, layer=0, longest=False):
     shape = W.config(name)
     lens = shape.context_lens
-    _say(f"decode full {name} lens={lens[0]}x{len(lens)} (sampled)")
+    _say(f"decode full {name} lens={lens[0]}..{max(lens)}x{len(lens)} (sampled)")
     s, plan, cache = _oracle_cache(shape, lens, layer=layer, fast=True)
     q = W.draw_q(s, layer=layer)
     got = _gpu_decode(s, plan, H.upload_cache(cache), q, lens)
     assert np.all(np.isfinite(got))
     rng = np.random.default_rng(99)
-    heads = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, s.batch, n_samples),
-                                                     rng.integers(0, s.num_q_heads, n_samples))})
+    heads = {(int(b), int(h)) for b, h in zip(rng.integers(0, s.batch, n_samples),
+                                              rng.integers(0, s.num_q_heads, n_samples))}
+    if longest:  # the sequence with the most splits, one head of each KV head's group
+        b_max = int(np.argmax(lens))
+        heads |= {(b_max, kvh * (s.num_q_heads // s.num_kv_heads)) for kvh in range(s.num_kv_heads)}
+    heads = sorted(heads)
     ref = O.decode(cache, q, plan.block_table, np.array(lens), s.num_kv_heads, s.hadamard_block, heads=heads)
     worst = H.check_attention(got, ref, f"full {name}", heads=heads)
     _say(f"  {len(heads)} sampled heads, worst rel-L2 {worst:.2e}")
@@ -184,3 +188,9 @@ def test_decode_full_llama2_70b_one_layer():
 
 def test_decode_full_oscar_int2():
     _full_size_sampled("oscar_int2", 8)
+
+
+def test_decode_full_sweep_b32():
+    # 32 ragged sequences x 8 KV heads fill the waves with few splits per sequence, so the planned
+    # splits are capped at 48 pages (the longest sequence, 7407 tokens, takes 10)
+    _full_size_sampled("sweep_b32", 8, longest=True)
