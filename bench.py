@@ -537,16 +537,23 @@ def suite_oscar(dev, stream, cpu):
         offs.append((o, o + len(sq)))
         o += len(sq)
     torch.cuda.synchronize()
+    # the short first chunks (1..15 tokens per sequence), then the 512-token chunks back to back as a
+    # serving loop issues them (each lands mid-page), timed together
+    full_calls = [i for i, (a, b) in enumerate(offs) if b - a == shape.batch * shape.chunk]
+    for i, ((a, b), sl) in enumerate(zip(offs, slot_list)):
+        if i not in full_calls:
+            kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale,
+                                       stream=stream)
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    chunk_ms = []
-    for (a, b), sl in zip(offs, slot_list):
-        e0.record(stream)
+    e0.record(stream)
+    for i in full_calls:
+        (a, b), sl = offs[i], slot_list[i]
         kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        chunk_ms.append(e0.elapsed_time(e1))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    chunk_mean_ms = e0.elapsed_time(e1) / max(1, len(full_calls))
     del k, v
-    full = [t for (a, b), t in zip(offs, chunk_ms) if b - a == shape.batch * shape.chunk]
     # attention cycles over 8 copies (1.3 GB) so that the 256 MB last-level cache cannot serve it
     copies = [cache] + [kvq.PagedKVCache(cache.k_codes.clone(), cache.v_codes.clone(), cache.k_sz.clone(),
                                          cache.v_sz.clone(), cache.bits) for _ in range(7)]
@@ -564,8 +571,8 @@ def suite_oscar(dev, stream, cpu):
                 bf16_attention_ms=round(t_bf, 5), bf16_attention_GBps=round(gb_bf, 1),
                 attention_speedup_vs_bf16=round(t_bf / t_att, 2),
                 cache_bytes_ratio_bf16=round(512 / (2 * 128 * shape.bits // 8 + 16), 2),
-                batch=shape.batch, chunk_appends=len(full), chunk_append_ms_median=round(float(np.median(full)), 5),
-                chunk_append_GBps=round(b_chunk / float(np.median(full)) / 1e6, 1), attention_ms=round(t_att, 5),
+                batch=shape.batch, chunk_appends=len(full_calls), chunk_append_ms_mean=round(chunk_mean_ms, 5),
+                chunk_append_GBps=round(b_chunk / chunk_mean_ms / 1e6, 1), attention_ms=round(t_att, 5),
                 attention_GBps=round(b_att / t_att / 1e6, 1), decode_token_append_ms=round(t_app, 5),
                 tokens_per_s=round(shape.batch / ((t_att + t_app) * 1e-3), 1))
     if cpu:
