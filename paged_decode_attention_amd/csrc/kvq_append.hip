@@ -253,10 +253,6 @@ __device__ __forceinline__ void process_tile(const AppendArgs& a, int64_t tile0,
   }
 }
 
-#ifndef KVQ_APPEND_HEAD_FASTEST
-#define KVQ_APPEND_HEAD_FASTEST 1
-#endif
-
 // One wave per work item of 16 tokens x one KV head, all loads issued before any arithmetic.
 // Items are numbered head-fastest (w = tile * H + h), so the waves that run together read the
 // same tokens' rows of all heads (one contiguous stretch of the K/V inputs) and write the
@@ -272,14 +268,8 @@ __global__ __launch_bounds__(256, KVQ_APPEND_MIN_WAVES) void append_kernel(const
   const int c = lane & 15;
   const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6);
   const uint32_t H = static_cast<uint32_t>(a.num_kv_heads);
-#if KVQ_APPEND_HEAD_FASTEST
   const int64_t tile = w / H;
   const int h = static_cast<int>(w % H);
-#else
-  const uint32_t tiles32 = static_cast<uint32_t>(num_tiles);
-  const int64_t tile = w % tiles32;
-  const int h = static_cast<int>(w / tiles32);
-#endif
   if (tile >= num_tiles || h >= a.num_kv_heads) return;  // uniform per wave
   const v4u bop[2] = {load_b<LB>(lane, 0), load_b<LB>(lane, 1)};
   TileInputs in;

@@ -34,12 +34,6 @@
 #ifndef KVQ_DECODE_MIN_WAVES
 #define KVQ_DECODE_MIN_WAVES 2    // waves per SIMD the register allocation must allow
 #endif
-#ifndef KVQ_DECODE_PACK
-// Most tiles whose scores share one QK output (1, 2 or 4). Two is the fastest measured on every
-// workload shape: four needs four-tile steps, and with only two step buffers in registers the
-// loads are covered by one step of work instead of two.
-#define KVQ_DECODE_PACK 2
-#endif
 
 namespace kvq {
 namespace {
@@ -184,19 +178,20 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + R, 0xF, 0xF, false));
 }
 
-// MQ = false: decode, one query per sequence. The 16 columns of the QK output are F tile slots of
-// W = 16 / F columns: column n holds query head n % W (used while below g) against the tokens of
-// tile n / W of the group, so one output carries the scores of F tiles and every lane's softmax
-// work is useful (F = 4 for g <= 4, 2 for g <= 8). The PV product then keeps one accumulator row
-// per (tile slot, head); the slots are summed once, at the end.
+// MQ = false: decode, one query per sequence. The 16 columns of the QK output are F = 2 tile slots
+// of W = 8 columns: column n holds query head n % W (used while below g <= 8) against the tokens
+// of tile n / W of the step, so one output carries the scores of both of the step's tiles and
+// every lane's softmax work is useful. The PV product then keeps one accumulator row per (tile
+// slot, head); the slots are summed once, at the end. (Four slots of four columns need four-tile
+// steps, which fit in registers only double-buffered; that was slower on every workload shape.)
 // MQ = true: several queries per sequence (F = 1); a wave takes a tile of 16 columns out of the
 // (query token, head) pairs of one KV head, column c meaning query c / g, head c % g, each with
 // its own causal length.
-// NT tiles per step: 4 with F = 4 (two step buffers), else 2 (three step buffers).
+// NT = 2 tiles per step, three step buffers.
 template <int BITS, bool PS16, int NT, bool MQ, int F>
 __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
-  static_assert(F == 1 || F == 2 || F == 4, "pack factor");
-  static_assert(NT % 2 == 0 && NT % F == 0, "a step holds whole PV chunks and whole packed groups");
+  static_assert(F == 1 || F == 2, "pack factor");
+  static_assert(NT == 2, "a step is one PV chunk of two tiles");
   static_assert(!MQ || F == 1, "several queries fill the 16 columns themselves");
   constexpr int W = 16 / F;   // columns per tile slot
   constexpr int KG = NT / F;  // packed score groups per step
@@ -463,8 +458,7 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 #pragma unroll
     for (int i = 1; i < P; ++i) mt = fmaxf(mt, sr[i]);
     mt = max_over_rows(mt);
-    if constexpr (F >= 2) mt = fmaxf(mt, row_ror<8>(mt));
-    if constexpr (F == 4) mt = fmaxf(mt, row_ror<4>(mt));
+    if constexpr (F == 2) mt = fmaxf(mt, row_ror<8>(mt));
     mt *= inv_scale;  // log2 units
     if (__any(mt > m_run + lazy)) {
       const float m_new = (mt > m_run + lazy) ? mt : m_run;
@@ -547,42 +541,30 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 #pragma unroll
   for (int u = 0; u < NT; ++u) reinterpret_cast<float*>(szs[0][u])[lane] = x0[u].sz;
   wave_lds_sync();
-  if constexpr (NT >= 4) {
-    // Double-buffered walk: while one step's tiles are processed, the next step's are loading.
-    for (int tile = tile_begin;; tile += 2 * NT) {
-      step(x0, pg0, tile, x1, 0);
-      if (tile + NT >= tile_end) break;
-      fetch(tile + 2 * NT, x0, pg0);
-      step(x1, pg1, tile + NT, x0, 1);
-      if (tile + 2 * NT >= tile_end) break;
-      fetch(tile + 3 * NT, x1, pg1);
-    }
-  } else {
-    // Triple-buffered walk: while the tiles of one buffer are processed, the next two steps'
-    // tiles are already loading. Step k reads scale/zero buffer k & 1; the six-step cycle keeps
-    // the parity aligned.
-    TileCodes x2[NT];
-    int64_t pg2[NT];
-    for (int tile = tile_begin;; tile += 6 * NT) {
-      fetch(tile + 2 * NT, x2, pg2);
-      step(x0, pg0, tile, x1, 0);
-      if (tile + NT >= tile_end) break;
-      fetch(tile + 3 * NT, x0, pg0);
-      step(x1, pg1, tile + NT, x2, 1);
-      if (tile + 2 * NT >= tile_end) break;
-      fetch(tile + 4 * NT, x1, pg1);
-      step(x2, pg2, tile + 2 * NT, x0, 0);
-      if (tile + 3 * NT >= tile_end) break;
-      fetch(tile + 5 * NT, x2, pg2);
-      step(x0, pg0, tile + 3 * NT, x1, 1);
-      if (tile + 4 * NT >= tile_end) break;
-      fetch(tile + 6 * NT, x0, pg0);
-      step(x1, pg1, tile + 4 * NT, x2, 0);
-      if (tile + 5 * NT >= tile_end) break;
-      fetch(tile + 7 * NT, x1, pg1);
-      step(x2, pg2, tile + 5 * NT, x0, 1);
-      if (tile + 6 * NT >= tile_end) break;
-    }
+  // Triple-buffered walk: while the tiles of one buffer are processed, the next two steps'
+  // tiles are already loading. Step k reads scale/zero buffer k & 1; the six-step cycle keeps
+  // the parity aligned.
+  TileCodes x2[NT];
+  int64_t pg2[NT];
+  for (int tile = tile_begin;; tile += 6 * NT) {
+    fetch(tile + 2 * NT, x2, pg2);
+    step(x0, pg0, tile, x1, 0);
+    if (tile + NT >= tile_end) break;
+    fetch(tile + 3 * NT, x0, pg0);
+    step(x1, pg1, tile + NT, x2, 1);
+    if (tile + 2 * NT >= tile_end) break;
+    fetch(tile + 4 * NT, x1, pg1);
+    step(x2, pg2, tile + 2 * NT, x0, 0);
+    if (tile + 3 * NT >= tile_end) break;
+    fetch(tile + 5 * NT, x2, pg2);
+    step(x0, pg0, tile + 3 * NT, x1, 1);
+    if (tile + 4 * NT >= tile_end) break;
+    fetch(tile + 6 * NT, x0, pg0);
+    step(x1, pg1, tile + 4 * NT, x2, 0);
+    if (tile + 5 * NT >= tile_end) break;
+    fetch(tile + 7 * NT, x1, pg1);
+    step(x2, pg2, tile + 5 * NT, x0, 1);
+    if (tile + 6 * NT >= tile_end) break;
   }
 
   // ---- finish: each head's totals over the row groups and the tile slots (then equal in every
@@ -591,13 +573,9 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   l_part += __shfl_xor(l_part, 32, 64);
   z_part += __shfl_xor(z_part, 16, 64);
   z_part += __shfl_xor(z_part, 32, 64);
-  if constexpr (F >= 2) {
+  if constexpr (F == 2) {
     l_part += row_ror<8>(l_part);
     z_part += row_ror<8>(z_part);
-  }
-  if constexpr (F == 4) {
-    l_part += row_ror<4>(l_part);
-    z_part += row_ror<4>(z_part);
   }
   // S output heads per lane: F = 1: heads 4G + s, straight from the accumulator rows; F > 1:
   // heads G + 4s, the sum of their F slot rows, exchanged through LDS.
@@ -796,17 +774,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const unsigned tiles = a.q_lens ? static_cast<unsigned>(mq_column_tiles(a.q_len_max, a.num_q_heads / a.num_kv_heads)) : 1u;
   const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
                   static_cast<unsigned>(a.batch));
-  hipError_t e;
-  const int g = a.num_q_heads / a.num_kv_heads;
-  if (a.q_lens) {
-    e = launch_kernel<true, 1, 2>(a, grid, stream);
-  } else if constexpr (KVQ_DECODE_PACK >= 4) {
-    e = (g <= 4) ? launch_kernel<false, 4, 4>(a, grid, stream) : launch_kernel<false, 2, 2>(a, grid, stream);
-  } else if constexpr (KVQ_DECODE_PACK == 2) {
-    e = launch_kernel<false, 2, 2>(a, grid, stream);  // g <= 8 (checked by the caller)
-  } else {
-    e = launch_kernel<false, 1, 2>(a, grid, stream);
-  }
+  // g <= 8 with one query per sequence (checked by the caller): two tile slots
+  const hipError_t e =
+      a.q_lens ? launch_kernel<true, 1, 2>(a, grid, stream) : launch_kernel<false, 2, 2>(a, grid, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   return launch_decode_merge(a, stream);
 }
