@@ -780,8 +780,12 @@ def main():
         print(summarize_sq(*args.summarize_sq, args.workload))
         return
     if args.summarize_kernel_stats:
-        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
-               f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
+        if args.suite_only:  # a trace of suite rows
+            cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
+                   f"--suite --suite-only {args.suite_only}")
+        else:
+            cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
+                   f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
         print(summarize_kernel_stats(args.summarize_kernel_stats, cmd))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
