@@ -184,7 +184,8 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
   const int b = blockIdx.z;
   const int g = a.num_q_heads / a.num_kv_heads;
   const int ps = a.page_size;
-  const int tpp = ps / 16;  // tiles per page (even)
+  const int tpp = ps / 16;  // tiles per page: 2, 4 or 8 (page sizes 32, 64, 128)
+  const int tpp_shift = (ps == 32) ? 1 : ((ps == 64) ? 2 : 3);  // tile indices are >= 0: shift and mask
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_full = len / ps;
   const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
@@ -238,9 +239,9 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
 #pragma unroll
     for (int u = 0; u < kNT; ++u) {
       const int tt = min(t + u, last_tile);
-      const int32_t p = page_id(tt / tpp);
+      const int32_t p = page_id(tt >> tpp_shift);
       pg[u] = (p >= 0 && t + u <= last_tile) ? p : -1;
-      const int64_t row0 = (p >= 0 ? p : 0) * page_rows + head_rows + 16 * (tt % tpp);
+      const int64_t row0 = (p >= 0 ? p : 0) * page_rows + head_rows + 16 * (tt & (tpp - 1));
       constexpr int kRowShift = (BITS == 4) ? 6 : 5;
       const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + (row0 << kRowShift), 16 << kRowShift);
       const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + (row0 << kRowShift), 16 << kRowShift);
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
   };
 
   auto step = [&](const PcTile (&c)[kNT], const int64_t (&pg)[kNT], int tile, const PcTile (&next)[kNT], int buf) {
-    const int p = tile / tpp;
-    if (tile % tpp == 0) page_begin(p);
+    const int p = tile >> tpp_shift;
+    if ((tile & (tpp - 1)) == 0) page_begin(p);
     v4i sc[kNT];
     {
       v4i s0[kNT], s1[kNT], s2[kNT];
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(64, 2) void pc_decode_kernel(const PcDecodeArgs a) 
       accp[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, accp[m], 0, 0, 0);
       accp[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, accp[m], 0, 0, 0);
     }
-    if ((tile + kNT) % tpp == 0) page_end(p);
+    if (((tile + kNT) & (tpp - 1)) == 0) page_end(p);
 #pragma unroll
     for (int u = 0; u < kNT; ++u) reinterpret_cast<float*>(szs[buf ^ 1][u])[lane] = next[u].s;
     wave_lds_sync();
