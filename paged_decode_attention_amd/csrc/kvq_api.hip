@@ -12,6 +12,11 @@ namespace {
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// A launch dimension holds fewer than 2^32 work-items (blocks x threads per block).
+bool grid_fits(int64_t blocks, int64_t threads_per_block) {
+  return blocks >= 0 && blocks <= (int64_t{0xFFFFFFFF} / threads_per_block);
+}
+
 kvq_status check_common(int32_t head_dim, int32_t page_size, int32_t hadamard_block, int32_t bits) {
   if (page_size <= 0 || hadamard_block <= 0) return KVQ_ERR_SHAPE;
   if (bits != 2 && bits != 4) return KVQ_ERR_UNSUPPORTED;
@@ -144,8 +149,9 @@ kvq_status kvq_rotate_quantize_append(
   const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (k_token_stride < row_elems || v_token_stride < row_elems) return KVQ_ERR_SHAPE;
   if (k_token_stride % 8 || v_token_stride % 8) return KVQ_ERR_SHAPE;
+  // one 64-lane wave per 16 tokens x one KV head, four per 256-thread workgroup
   if (num_kv_heads > 65535 || num_tokens > (int64_t{1} << 36) ||
-      ((num_tokens + 15) / 16) * num_kv_heads > 0x7FFFFFFF)
+      !grid_fits((((num_tokens + 15) / 16) * num_kv_heads + 3) / 4, 256))
     return KVQ_ERR_UNSUPPORTED;
   // 32-bit slots and rows per page
   if (static_cast<int64_t>(num_pages) * page_size > 0xFFFFFFFFll ||
@@ -224,13 +230,17 @@ kvq_status decode_args(
   const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
+  const kvq::SplitPlan plan =
+      kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, q_len_max == 0);
+  // one 64-lane wave per split (x) and per merged (query row, head) pair
+  if (!grid_fits(plan.num_splits, 64) ||
+      !grid_fits(static_cast<int64_t>(batch) * (q_len_max > 0 ? q_len_max : 1) * num_q_heads, 64))
+    return KVQ_ERR_UNSUPPORTED;
   if (!q || !k_codes || !v_codes || !k_sz || !v_sz || !block_table || !context_lens || !out) return KVQ_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(k_sz, 8) ||
       !aligned(v_sz, 8) || !aligned(block_table, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_SHAPE;
 
-  const kvq::SplitPlan plan =
-      kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, q_len_max == 0);
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads, q_len_max > 0 ? q_len_max : 1);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
 
@@ -406,7 +416,7 @@ kvq_status kvq_bf16_cache_write(
   const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (k_token_stride < row_elems || v_token_stride < row_elems || k_token_stride % 8 || v_token_stride % 8)
     return KVQ_ERR_SHAPE;
-  if (num_kv_heads > 65535 || (num_tokens + 15) / 16 > 0x7FFFFFFF) return KVQ_ERR_UNSUPPORTED;
+  if (num_kv_heads > 65535 || !grid_fits((num_tokens + 15) / 16, 256)) return KVQ_ERR_UNSUPPORTED;
   if (num_tokens == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return KVQ_ERR_NULL;
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8) || !aligned(k_cache, 16) ||
@@ -444,11 +454,13 @@ kvq_status kvq_paged_decode_attention_bf16(
   const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
+  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
+  if (!grid_fits(plan.num_splits, 64) || !grid_fits(static_cast<int64_t>(batch) * num_q_heads, 64))
+    return KVQ_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return KVQ_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
     return KVQ_ERR_SHAPE;
-  const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
   kvq::DecodeBf16Args a{};
@@ -505,8 +517,7 @@ kvq_status kvq_pc_write_pages(
   if (num_input_pages < 0 || num_kv_heads <= 0 || num_pages < 0) return KVQ_ERR_SHAPE;
   if (kvq_status s = check_pc(head_dim, page_size, hadamard_block, bits)) return s;
   // one workgroup of 4 page_size threads per (input page, KV head), in one grid dimension
-  if (static_cast<int64_t>(num_input_pages) * num_kv_heads * 4 * page_size >= (int64_t{1} << 32))
-    return KVQ_ERR_UNSUPPORTED;
+  if (!grid_fits(static_cast<int64_t>(num_input_pages) * num_kv_heads, 4 * page_size)) return KVQ_ERR_UNSUPPORTED;
   const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
   if (k_token_stride < row_elems || v_token_stride < row_elems || k_token_stride % 8 || v_token_stride % 8)
     return KVQ_ERR_SHAPE;
@@ -564,6 +575,11 @@ kvq_status kvq_pc_decode_attention(
   if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
   if (max_pages_per_seq < max_context_len / page_size) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
+  const kvq::SplitPlan plan = pc_plan(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
+  // one wave per page split plus the tail's, and per merged (sequence, head) pair
+  if (!grid_fits(static_cast<int64_t>(plan.num_splits) + 1, 64) ||
+      !grid_fits(static_cast<int64_t>(batch) * num_q_heads, 64))
+    return KVQ_ERR_UNSUPPORTED;
   if (!q || !k_codes || !v_codes || !k_s || !v_s || !k_cp || !v_cp || !block_table || !context_lens || !tail_k ||
       !tail_v || !out)
     return KVQ_ERR_NULL;
@@ -571,7 +587,6 @@ kvq_status kvq_pc_decode_attention(
       !aligned(v_s, 4) || !aligned(k_cp, 16) || !aligned(v_cp, 16) || !aligned(block_table, 4) ||
       !aligned(context_lens, 4) || !aligned(tail_k, 16) || !aligned(tail_v, 16))
     return KVQ_ERR_SHAPE;
-  const kvq::SplitPlan plan = pc_plan(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
   const WorkspaceLayout ws = workspace_layout(plan.num_splits + 1, batch, num_q_heads);
   if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
   kvq::PcDecodeArgs a{};

@@ -254,3 +254,17 @@ def test_pc_validation_and_workspace():
     assert ws(2, 32, 8, 128, 4096, 64, 0) > ws(2, 32, 8, 128, 4096, 64, 64)
     assert ws(2, 32, 8, 128, 4096, 64, 64) == 2 * 2 * 32 * 128 * 4 + 1024   # 128 rows of (max, sum)
     assert ws(0, 32, 8, 128, 4096, 64, 0) == 0
+
+
+def test_launch_grid_limits():
+    # a launch dimension holds fewer than 2^32 work-items: larger sizes are refused before any
+    # pointer is looked at (NULL pointers below), sizes just inside pass on to the pointer checks
+    # append: one 64-lane wave per (16-token tile, KV head) item, four items per 256-thread workgroup
+    assert _append(n=16 * (1 << 24), h=4, ks=512, vs=512) == kvq.KVQ_ERR_UNSUPPORTED            # 2^26 items
+    assert _append(n=16 * ((1 << 24) - 1), h=4, ks=512, vs=512) == kvq.KVQ_ERR_NULL             # 2^26 - 4
+    # decode: one wave per split (here one page per split) and one merge wave per (sequence, head)
+    big = 16 * (1 << 26)  # 2^26 pages of 16 tokens
+    assert _decode(mcl=big - 16, mpps=1 << 26, pps=1, pages=1 << 26) == kvq.KVQ_ERR_NULL        # 2^26 - 1 splits
+    assert _decode(mcl=big, mpps=1 << 26, pps=1, pages=1 << 26) == kvq.KVQ_ERR_UNSUPPORTED      # 2^26 splits
+    assert _decode(b=65535, hq=1025, hkv=205, mcl=64, mpps=4) == kvq.KVQ_ERR_UNSUPPORTED          # > 2^26 pairs
+    assert _decode(b=65535, hq=1020, hkv=204, mcl=64, mpps=4) == kvq.KVQ_ERR_NULL                 # < 2^26 pairs
