@@ -117,6 +117,15 @@ def _dev(t: torch.Tensor, name: str, dtype) -> int:
     return t.data_ptr()
 
 
+def _workspace(workspace):
+    """(pointer, bytes) of a caller's workspace: a contiguous device tensor of any dtype, or None."""
+    if workspace is None:
+        return None, 0
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device (cuda/hip) tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 # ----------------------------------------------------------------------------- cache
 
 @dataclass
@@ -220,8 +229,7 @@ def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: to
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
         workspace = decode_workspace(need, q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_decode_attention(
         _dev(q, "q", torch.bfloat16), q_prerotated,
         _dev(cache.k_codes, "k_codes", torch.uint8), _dev(cache.v_codes, "v_codes", torch.uint8),
@@ -264,8 +272,7 @@ def paged_prefill_attention(q: torch.Tensor, q_lens: torch.Tensor, cache: PagedK
                                   pages_per_split)
     if workspace is None and need > 0:
         workspace = decode_workspace(need, q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_prefill_attention(
         _dev(q, "q", torch.bfloat16), q_prerotated, _dev(q_lens, "q_lens", torch.int32), qmax,
         _dev(cache.k_codes, "k_codes", torch.uint8), _dev(cache.v_codes, "v_codes", torch.uint8),
@@ -304,8 +311,7 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
         workspace = decode_workspace(need, q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_decode_step(
         _dev(q, "q", torch.bfloat16), q_prerotated, _dev(k_new, "k_new", torch.bfloat16),
         _dev(v_new, "v_new", torch.bfloat16), k_new.stride(0), v_new.stride(0),
@@ -407,8 +413,7 @@ def paged_decode_attention_bf16(q: torch.Tensor, cache: PagedKVCacheBF16, block_
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
         workspace = decode_workspace(need, q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_decode_attention_bf16(
         _dev(q, "q", torch.bfloat16), _dev(cache.k, "k_cache", torch.bfloat16), _dev(cache.v, "v_cache", torch.bfloat16),
         cache.num_pages, cache.page_size, _dev(block_table, "block_table", torch.int32), block_table.shape[1],
@@ -531,6 +536,6 @@ def pc_decode_attention(q: torch.Tensor, cache: PagedKVCachePC, block_table: tor
         _dev(context_lens, "context_lens", torch.int32), max_context_len,
         _dev(tail_k, "tail_k", torch.bfloat16), _dev(tail_v, "tail_v", torch.bfloat16), bsz, hq,
         cache.num_kv_heads, HEAD_DIM, hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream))
+        *_workspace(workspace), pages_per_split, _stream(stream))
     _check(st, "kvq_pc_decode_attention")
     return out

@@ -149,6 +149,10 @@ def test_binding_refuses_host_tensors():
     c = kvq.PagedKVCache.empty(4, 2, 16, 4, device="cpu")
     with pytest.raises(ValueError):
         kvq.dequant_page(c, "k", 0, 32)
+    # a caller's workspace must be device memory too (its pointer goes to the kernels)
+    with pytest.raises(ValueError):
+        kvq._workspace(torch.empty(64, dtype=torch.uint8))
+    assert kvq._workspace(None) == (None, 0)
 
 
 def test_bf16_baseline_validation():
