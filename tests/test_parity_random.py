@@ -82,3 +82,81 @@ def test_random_configuration(i):
         if lens[bb] == 0:
             assert np.all(got[bb] == 0), f"case {i}: empty sequence {bb} gives a nonzero output"
     _say(f"  case {i}: worst rel-L2 {worst:.2e}")
+
+
+def _prefix_cache(shape, lens_prev):
+    """The oracle's cache holding each sequence's first lens_prev[b] tokens (room for one more)."""
+    s = shape.with_(context_lens=tuple(lens_prev))
+    plan = W.plan_pages(s, extra_tokens=1)
+    seq, pos = W.prefill_order(s)
+    k, v = W.draw_kv(s, len(seq))
+    cache = O.PagedCache(plan.num_pages, s.num_kv_heads, s.page_size, 128, s.bits)
+    slots = W.slots_for_positions(plan, s.page_size, seq, pos)
+    diag = O.append(cache, k, v, slots, s.hadamard_block, s.token_scale)
+    return s, plan, cache, [(slots, diag)]
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2))
+def test_random_decode_step(i):
+    """The fused decode step (append each sequence's newest token, then attend) against the oracle's
+    append followed by its decode: the attention and the whole cache afterwards."""
+    shape, pps = _config(i)
+    lens = np.array(shape.context_lens, dtype=np.int64)  # with the new token
+    _say(f"random decode step {i}: lens {tuple(lens)}, heads {shape.num_q_heads}/{shape.num_kv_heads}, "
+         f"page {shape.page_size}, INT{shape.bits}, token scale {shape.token_scale}, block {shape.hadamard_block}, "
+         f"pages_per_split {pps}")
+    s, plan, cache, diags = _prefix_cache(shape, np.maximum(lens - 1, 0))
+    dev = H.upload_cache(cache)
+    kn, vn = W.draw_kv(s, s.batch, stream="decode")
+    live = lens > 0
+    new_slots = W.slots_for_positions(plan, s.page_size, np.arange(s.batch), np.maximum(lens - 1, 0))
+    new_slots = np.where(live, new_slots, -1).astype(np.int64)
+    diags.append((new_slots, O.append(cache, kn, vn, new_slots, s.hadamard_block, s.token_scale)))
+    q = W.draw_q(s)
+    want = O.decode(cache, q, plan.block_table, lens, s.num_kv_heads, s.hadamard_block)
+    max_len = int(lens.max())
+    nbytes = kvq.decode_workspace_size(s.batch, s.num_q_heads, s.num_kv_heads, max_len, s.page_size, pps)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    got = kvq.decode_step(H.to_dev_bf16(q), H.to_dev_bf16(kn), H.to_dev_bf16(vn), dev, H.to_dev(plan.block_table),
+                          H.to_dev(lens.astype(np.int32)), max_len, s.hadamard_block, token_scale=s.token_scale,
+                          workspace=ws, pages_per_split=pps)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    heads = [(bb, h) for bb in range(s.batch) if lens[bb] > 0 for h in range(s.num_q_heads)]
+    worst = H.check_attention(got, want, f"step {i}", heads=heads)
+    assert all(np.all(got[bb] == 0) for bb in range(s.batch) if lens[bb] == 0), f"step {i}: empty sequence"
+    compare_caches(H.download_cache(dev), cache, diags, f"step {i}")
+    _say(f"  step {i}: worst rel-L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("i", range(N_CASES // 2, N_CASES))
+def test_random_multi_query(i):
+    """Several queries per sequence (causal, each sequence's last q_lens[b] tokens) against the
+    oracle's multi-query attention; rows past a sequence's queries are zero."""
+    shape, pps = _config(i)
+    r = np.random.default_rng(9000 + i)
+    lens = np.array(shape.context_lens, dtype=np.int64)
+    q_lens = np.array([int(r.integers(0, min(n, 24) + 1)) for n in lens], dtype=np.int32)
+    qmax = max(1, int(q_lens.max()))
+    _say(f"random multi-query {i}: lens {tuple(lens)}, q_lens {tuple(q_lens)}, heads {shape.num_q_heads}/"
+         f"{shape.num_kv_heads}, page {shape.page_size}, INT{shape.bits}, block {shape.hadamard_block}, "
+         f"pages_per_split {pps}")
+    s, plan, cache, _ = _prefix_cache(shape, lens)
+    q = W.f32_to_bf16_bits(r.standard_normal((s.batch, qmax, s.num_q_heads, 128)).astype(np.float32))
+    want = O.multi_query_attention(cache, q, q_lens, plan.block_table, lens, s.num_kv_heads, s.hadamard_block)
+    max_len = int(lens.max())
+    nbytes = kvq.prefill_workspace_size(s.batch, qmax, s.num_q_heads, s.num_kv_heads, max_len, s.page_size, pps)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    got = kvq.paged_prefill_attention(H.to_dev_bf16(q), H.to_dev(q_lens), H.upload_cache(cache),
+                                      H.to_dev(plan.block_table), H.to_dev(lens.astype(np.int32)), max_len,
+                                      s.hadamard_block, workspace=ws, pages_per_split=pps)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    rows = [(bb, j, h) for bb in range(s.batch) for j in range(int(q_lens[bb])) for h in range(s.num_q_heads)]
+    if rows:
+        idx = tuple(np.array(rows).T)
+        e = H.rel_l2(got[idx], want[idx])
+        assert np.all(np.isfinite(got[idx])) and e.max() <= H.ATTN_RTOL, f"multi-query {i}: worst rel-L2 {e.max():.3e}"
+        _say(f"  multi-query {i}: {len(rows)} rows, worst rel-L2 {e.max():.2e}")
+    for bb in range(s.batch):
+        assert np.all(got[bb, int(q_lens[bb]):] == 0), f"multi-query {i}: rows past sequence {bb}'s queries"
