@@ -23,7 +23,7 @@ It is the plain definition of what the method computes, written out slowly with 
   with a causal limit per query: the paged low-bit attention of the OSCAR abstract applied to the
   prefill side.
 * Per-channel pages (``PagedCachePC``, ``write_pages_pc``, ``decode_pc``) -- the per-channel
-  reading of OScaR (OScaR abstract on the openalex page: "advancing the per-channel paradigm";
+  reading of OScaR (OScaR abstract on the openalex page: the method moves per-channel quantization forward;
   zhichai.net summary, "Root Cause: Token Norm Imbalance" and "The OScaR Framework"): per-token
   scaling after the rotation, then one (scale, zero) per channel shared by the tokens of a page;
   a sequence's unfinished last page stays in bf16 until it is complete.
