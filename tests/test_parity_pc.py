@@ -260,3 +260,37 @@ def test_pc_decode_sampled_large():
     rng = np.random.default_rng(9)
     heads = [(int(b), int(h)) for b, h in zip(rng.integers(0, 16, 12), rng.integers(0, 32, 12))]
     _decode_case("llama3_8b-sized", shape, ps, 2, 128, [0], seed=11, heads=heads)
+
+
+def _pc_random_config(i):
+    r = np.random.default_rng(8000 + i)
+    ps = int(r.choice([32, 64, 128]))
+    bits = int(r.choice([2, 4]))
+    hb = int(2 ** int(r.integers(0, 8)))
+    kvh = int(r.choice([1, 2, 4]))
+    g = int(r.integers(1, 9))
+    b = int(r.integers(1, 4))
+    lens = [int(n) if r.random() > 0.15 else 0 for n in r.integers(1, 4 * ps, size=b)]
+    if max(lens) == 0:
+        lens[0] = int(r.integers(1, 4 * ps))
+    pps = int(r.choice([0, 1, 2, 1000]))
+    shape = W.config("oscar_int2", batch=b, num_q_heads=kvh * g, num_kv_heads=kvh,
+                     seed=8000 + i).with_(context_lens=tuple(lens))
+    return shape, ps, bits, hb, pps
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_pc_random_configuration(i):
+    """Seeded random shapes (page size, width, block size, heads, group size, ragged lengths with
+    tails and empty sequences, split size): the GPU page writer against the oracle's pages, then the
+    GPU decode over the oracle's pages and tails against the oracle's decode."""
+    shape, ps, bits, hb, pps = _pc_random_config(i)
+    _say(f"pc random {i}: lens {shape.context_lens}, heads {shape.num_q_heads}/{shape.num_kv_heads}, page {ps}, "
+         f"INT{bits}, block {hb}, pages_per_split {pps}")
+    c = _case(shape, ps, bits, hb, seed=8000 + i)
+    if len(c["ids"]):
+        dev = _poisoned(c["cache"].num_pages, shape.num_kv_heads, ps, bits)
+        kvq.pc_write_pages(H.to_dev_bf16(c["pk"]), H.to_dev_bf16(c["pv"]), H.to_dev(c["ids"]), dev, hb)
+        torch.cuda.synchronize()
+        _compare_pc_caches(_download(dev), c["cache"], c["ids"], c["diag"], f"random {i}")
+    _decode_case(f"random {i}", shape, ps, bits, hb, [pps], seed=8000 + i)
