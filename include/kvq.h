@@ -40,8 +40,9 @@
  *   - head_dim must be 128 and page_size a multiple of 16 (KVQ_ERR_UNSUPPORTED otherwise).
  *   - Sizes whose launch would need 2^32 or more work-items in one grid dimension return
  *     KVQ_ERR_UNSUPPORTED: an append of more than 2^26 - 4 (16-token tile, KV head) items
- *     (about a billion token-heads), 2^26 or more splits of one sequence, or 2^26 or more
- *     (query row, head) pairs in one attention call.
+ *     (about a billion token-heads), 2^26 or more (split, sequence, KV head) waves in a decode
+ *     (splits of one sequence times sequences times KV heads), or 2^26 or more (query row, head)
+ *     pairs in one attention call.
  *   - Alignment (KVQ_ERR_SHAPE otherwise): k, v, q, out, k_codes and v_codes 16 bytes (the
  *     codes argument of kvq_dequant_page 4); slot_mapping, k_sz, v_sz 8; block_table and
  *     context_lens 4; token strides a multiple of 8 elements.

@@ -232,8 +232,9 @@ kvq_status decode_args(
   if (batch == 0) return KVQ_OK;
   const kvq::SplitPlan plan =
       kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, q_len_max == 0);
-  // one 64-lane wave per split (x) and per merged (query row, head) pair
-  if (!grid_fits(plan.num_splits, 64) ||
+  // one 64-lane wave per split and (sequence, KV head) item (one grid dimension with one query per
+  // sequence), and per merged (query row, head) pair
+  if (!grid_fits(static_cast<int64_t>(plan.num_splits) * (q_len_max > 0 ? 1 : static_cast<int64_t>(batch) * num_kv_heads), 64) ||
       !grid_fits(static_cast<int64_t>(batch) * (q_len_max > 0 ? q_len_max : 1) * num_q_heads, 64))
     return KVQ_ERR_UNSUPPORTED;
   if (!q || !k_codes || !v_codes || !k_sz || !v_sz || !block_table || !context_lens || !out) return KVQ_ERR_NULL;

@@ -206,10 +206,17 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   const int n = lane & 15;
   const int u_l = n / W;  // tile slot of this lane's column
   const int h_l = n % W;  // query column of this lane
-  const int split = blockIdx.x;
-  const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads) : static_cast<int>(blockIdx.y);
+  // One query per sequence: a one-dimensional grid numbered (sequence, KV head) item fastest, so
+  // that with a multiple of 8 items every split of an item lands on the same XCD (workgroups go to
+  // the eight XCDs in turn) - and the merge of its partials, numbered alike, reads them from that
+  // XCD's L2.
+  const uint32_t items = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads);
+  const uint32_t item = MQ ? 0u : blockIdx.x % items;
+  const int split = MQ ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x / items);
+  const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads)
+                     : static_cast<int>(item % static_cast<uint32_t>(a.num_kv_heads));
   const int c0 = MQ ? 16 * static_cast<int>(blockIdx.y / a.num_kv_heads) : 0;  // first column of the tile
-  const int b = blockIdx.z;
+  const int b = MQ ? static_cast<int>(blockIdx.z) : static_cast<int>(item / static_cast<uint32_t>(a.num_kv_heads));
   const int g = a.num_q_heads / a.num_kv_heads;
   const int ps = PS16 ? 16 : a.page_size;
   const int tiles_per_page = PS16 ? 1 : ps / 16;
@@ -673,7 +680,15 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
-  const uint32_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
+  // one query per sequence: numbered like the decode's items (item fastest, then the group's head)
+  uint32_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
+  if (!a.q_lens) {
+    const uint32_t items = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads);
+    const uint32_t gq = static_cast<uint32_t>(a.num_q_heads / a.num_kv_heads);
+    const uint32_t item = blockIdx.x % items, j = blockIdx.x / items;
+    const uint32_t bb = item / static_cast<uint32_t>(a.num_kv_heads), kk = item % static_cast<uint32_t>(a.num_kv_heads);
+    pair = bb * static_cast<uint32_t>(a.num_q_heads) + kk * gq + j;
+  }
   const int q_len_max = a.q_lens ? a.q_len_max : 1;
   const int64_t pairs = static_cast<int64_t>(a.batch) * q_len_max * a.num_q_heads;
   const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
@@ -772,8 +787,10 @@ int32_t mq_column_tiles(int32_t q_len_max, int32_t group) { return (q_len_max * 
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const unsigned tiles = a.q_lens ? static_cast<unsigned>(mq_column_tiles(a.q_len_max, a.num_q_heads / a.num_kv_heads)) : 1u;
-  const dim3 grid(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
-                  static_cast<unsigned>(a.batch));
+  const dim3 grid = a.q_lens ? dim3(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
+                                    static_cast<unsigned>(a.batch))
+                             : dim3(static_cast<unsigned>(a.num_splits) * static_cast<unsigned>(a.batch) *
+                                    static_cast<unsigned>(a.num_kv_heads));
   // g <= 8 with one query per sequence (checked by the caller): two tile slots
   const hipError_t e =
       a.q_lens ? launch_kernel<true, 1, 2>(a, grid, stream) : launch_kernel<false, 2, 2>(a, grid, stream);

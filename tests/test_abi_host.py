@@ -266,9 +266,12 @@ def test_launch_grid_limits():
     # append: one 64-lane wave per (16-token tile, KV head) item, four items per 256-thread workgroup
     assert _append(n=16 * (1 << 24), h=4, ks=512, vs=512) == kvq.KVQ_ERR_UNSUPPORTED            # 2^26 items
     assert _append(n=16 * ((1 << 24) - 1), h=4, ks=512, vs=512) == kvq.KVQ_ERR_NULL             # 2^26 - 4
-    # decode: one wave per split (here one page per split) and one merge wave per (sequence, head)
+    # decode: one wave per (split, sequence, KV head) (here one page per split) and one merge wave
+    # per (sequence, head)
     big = 16 * (1 << 26)  # 2^26 pages of 16 tokens
-    assert _decode(mcl=big - 16, mpps=1 << 26, pps=1, pages=1 << 26) == kvq.KVQ_ERR_NULL        # 2^26 - 1 splits
-    assert _decode(mcl=big, mpps=1 << 26, pps=1, pages=1 << 26) == kvq.KVQ_ERR_UNSUPPORTED      # 2^26 splits
+    one = dict(b=1, hq=4, hkv=1, mpps=1 << 26, pps=1, pages=1 << 26)
+    assert _decode(mcl=big - 16, **one) == kvq.KVQ_ERR_NULL                                       # 2^26 - 1 splits
+    assert _decode(mcl=big, **one) == kvq.KVQ_ERR_UNSUPPORTED                                     # 2^26 splits
+    assert _decode(mcl=16 * (1 << 22), mpps=1 << 22, pps=1, pages=1 << 22) == kvq.KVQ_ERR_UNSUPPORTED  # 2^22 x 16 items
     assert _decode(b=65535, hq=1025, hkv=205, mcl=64, mpps=4) == kvq.KVQ_ERR_UNSUPPORTED          # > 2^26 pairs
     assert _decode(b=65535, hq=1020, hkv=204, mcl=64, mpps=4) == kvq.KVQ_ERR_NULL                 # < 2^26 pairs
