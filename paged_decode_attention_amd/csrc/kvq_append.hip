@@ -23,7 +23,7 @@
 // Quantization of the 32 values a lane holds per tensor: min / max in-lane and across the 16-lane
 // row (DPP), scale and its reciprocal computed once per token (lane c & 3 does token c & 3, then
 // quad broadcasts), codes by Markstein-corrected division (bit-exact with IEEE division), round
-// half to even. Tokens whose scale is 0 or tiny take a slower path with IEEE division and the
+// half to even inside the byte conversion of the packing. Tokens whose scale is 0 or tiny take a slower path with IEEE division and the
 // clamp; it is wave-uniform and never taken for ordinary data.
 #include <algorithm>
 
@@ -35,7 +35,36 @@
 namespace kvq {
 namespace {
 
-constexpr float kFastMinScale = 0x1p-100f;  // below this (or 0) a token takes the guarded path
+// A token whose scale lies outside [2^-100, 2^101) (0, tiny, huge or not finite) takes the guarded
+// path; inside it the reciprocal from rcp_rn is the correctly rounded one that div_rn needs.
+constexpr float kFastMinScale = 0x1p-100f;
+constexpr float kFastMaxScale = 0x1p101f;
+
+// Pack the 8 codes of one token (channels 8c .. 8c + 7), given as floats in [0, qmax + 1/2), into
+// INT4 nibbles (4 bytes, even channel in the low nibble) or INT2 crumbs (2 bytes, lowest channel
+// in the low bits). v_cvt_pk_u8_f32 rounds half to even, the same as rintf on every float in
+// [0, 16) (checked exhaustively on gfx950), so the rounding to an integer code happens inside the
+// conversion and the codes are then merged with shifts.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_codes(const float (&cd)[8]) {
+  if constexpr (BITS == 4) {
+    uint32_t ev = 0, od = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      ev = __builtin_amdgcn_cvt_pk_u8_f32(cd[2 * m], m, ev);
+      od = __builtin_amdgcn_cvt_pk_u8_f32(cd[2 * m + 1], m, od);
+    }
+    return ev | (od << 4);
+  } else {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = __builtin_amdgcn_cvt_pk_u8_f32(cd[j], 0, w[j]);
+      w[j] = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 + j], 1, w[j]);
+    }
+    return w[0] | (w[1] << 2) | (w[2] << 4) | (w[3] << 6);
+  }
+}
 
 // Quantize and pack the 32 values y[n][i] (token i, channel 8c + n) of one tensor. Returns the
 // packed codes of each token (INT4: 4 bytes, INT2: 2 bytes) and its stored scale and zero.
@@ -98,7 +127,8 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   const float d_own = pick4(own, mx[0] - mn[0], mx[1] - mn[1], mx[2] - mn[2], mx[3] - mn[3]);
   constexpr float kInvQmax = 1.0f / kQmax;
   const float delta_own = div_rn(d_own, kQmax, kInvQmax);
-  const float r_own = 1.0f / delta_own;
+  const bool fast_own = delta_own >= kFastMinScale && delta_own < kFastMaxScale;
+  const float r_own = rcp_rn(fast_own ? delta_own : 1.0f);
   float delta[4], r[4];
   delta[0] = quad_bcast<0>(delta_own); r[0] = quad_bcast<0>(r_own);
   delta[1] = quad_bcast<1>(delta_own); r[1] = quad_bcast<1>(r_own);
@@ -106,26 +136,15 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   delta[3] = quad_bcast<3>(delta_own); r[3] = quad_bcast<3>(r_own);
 
   // every token of the wave is some lane's own token
-  if (__builtin_expect(__all(delta_own >= kFastMinScale), 1)) {
-    // q = RN((y - mn) / delta) exactly; q <= qmax (1 + 2^-23) and q >= 0, so rint needs no clamp.
+  if (__builtin_expect(__all(fast_own), 1)) {
+    // q = RN((y - mn) / delta) exactly; q <= qmax (1 + 2^-23) and q >= 0, so the rounding to an
+    // integer in the packing needs no clamp.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float cd[8];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) cd[n] = rintf(div_rn(y[n][i] - mn[i], delta[i], r[i]));
-      uint32_t p = 0;
-      if constexpr (BITS == 4) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) p = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(cd[2 * m + 1], 16.0f, cd[2 * m]), m, p);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(cd[4 * m + 3], 4.0f, cd[4 * m + 2]), 4.0f,
-                                                         cd[4 * m + 1]), 4.0f, cd[4 * m]);
-          p = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, p);
-        }
-      }
-      packed[i] = p;
+      for (int n = 0; n < 8; ++n) cd[n] = div_rn(y[n][i] - mn[i], delta[i], r[i]);
+      packed[i] = pack_codes<BITS>(cd);
     }
   } else {
     // Guarded path: IEEE division, the clamp, and all-zero codes for a zero scale.
@@ -136,19 +155,7 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
 #pragma unroll
       for (int n = 0; n < 8; ++n)
         cd[n] = (delta[i] != 0.0f) ? fminf(fmaxf(rintf((y[n][i] - mn[i]) / delta[i]), 0.0f), kQmax) : 0.0f;
-      uint32_t p = 0;
-      if constexpr (BITS == 4) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) p = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(cd[2 * m + 1], 16.0f, cd[2 * m]), m, p);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(cd[4 * m + 3], 4.0f, cd[4 * m + 2]), 4.0f,
-                                                         cd[4 * m + 1]), 4.0f, cd[4 * m]);
-          p = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, p);
-        }
-      }
-      packed[i] = p;
+      packed[i] = pack_codes<BITS>(cd);
     }
   }
 #pragma unroll
