@@ -40,32 +40,6 @@ namespace {
 constexpr float kFastMinScale = 0x1p-100f;
 constexpr float kFastMaxScale = 0x1p101f;
 
-// Pack the 8 codes of one token (channels 8c .. 8c + 7), given as floats in [0, qmax + 1/2), into
-// INT4 nibbles (4 bytes, even channel in the low nibble) or INT2 crumbs (2 bytes, lowest channel
-// in the low bits). v_cvt_pk_u8_f32 rounds half to even, the same as rintf on every float in
-// [0, 16) (checked exhaustively on gfx950), so the rounding to an integer code happens inside the
-// conversion and the codes are then merged with shifts.
-template <int BITS>
-__device__ __forceinline__ uint32_t pack_codes(const float (&cd)[8]) {
-  if constexpr (BITS == 4) {
-    uint32_t ev = 0, od = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      ev = __builtin_amdgcn_cvt_pk_u8_f32(cd[2 * m], m, ev);
-      od = __builtin_amdgcn_cvt_pk_u8_f32(cd[2 * m + 1], m, od);
-    }
-    return ev | (od << 4);
-  } else {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[j] = __builtin_amdgcn_cvt_pk_u8_f32(cd[j], 0, w[j]);
-      w[j] = __builtin_amdgcn_cvt_pk_u8_f32(cd[4 + j], 1, w[j]);
-    }
-    return w[0] | (w[1] << 2) | (w[2] << 4) | (w[3] << 6);
-  }
-}
-
 // Quantize and pack the 32 values y[n][i] (token i, channel 8c + n) of one tensor. Returns the
 // packed codes of each token (INT4: 4 bytes, INT2: 2 bytes) and its stored scale and zero.
 template <int BITS, bool TOKEN_SCALE, bool ODD_LB>

@@ -109,21 +109,12 @@ __device__ __forceinline__ uint32_t rotate_quantize_row(float (&x)[8], const Row
   uint32_t packed = 0;
   if (delta != 0.0f) {
     const float r = 1.0f / delta;
+    // clamped to [0, qmax] before the packing rounds to an integer: the same codes as rounding first,
+    // since both bounds are integers
     float c[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(rintf(div_rn(x[k] - mn, delta, r)), 0.0f), kQmax);
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        packed = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[2 * m + 1], 16.0f, c[2 * m]), m, packed);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(c[4 * m + 3], 4.0f, c[4 * m + 2]), 4.0f,
-                                                       c[4 * m + 1]), 4.0f, c[4 * m]);
-        packed = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, packed);
-      }
-    }
+    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(div_rn(x[k] - mn, delta, r), 0.0f), kQmax);
+    packed = pack_codes<BITS>(c);
   }
   scale = delta * s;
   zero = mn * s;
