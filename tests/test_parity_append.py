@@ -177,3 +177,45 @@ def test_append_full_llama3_8b_prefill():
         H.check_scale_zero(sz[pg, :, of, 0], sz[pg, :, of, 1], sc, zr, 4, f"full {name}")
     assert np.array_equal(np.isnan(got.k_sz), np.isnan(ref.k_sz))
     _say(f"  full prefill: {live.sum() * 8 * 2 * 128} elements, boundary mismatches {n_bad}")
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_append_rounding_ties_exact(bits):
+    """Codes that fall exactly halfway between two integers round to the even one, on the GPU as in
+    the oracle, with no boundary allowance. With a Hadamard block of 1 the rotation is the identity,
+    and a token whose values span exactly [o, o + qmax] * 2^e has the scale 2^e and the zero o * 2^e,
+    so (y - zero) / scale is the token's pattern value itself: the expected codes are rint of the
+    pattern (half to even), a closed form independent of the oracle."""
+    qmax = 2 ** bits - 1
+    rng = np.random.default_rng(31 + bits)
+    t_n, h_n = 32, 2
+    ties = [k + 0.5 for k in range(qmax)]
+    base = np.array([0.0, float(qmax)] + ties, dtype=np.float64)
+    quarters = rng.integers(0, 4 * qmax + 1, size=(t_n, h_n, 2, 128 - base.size)) / 4.0
+    pattern = np.concatenate([np.broadcast_to(base, (t_n, h_n, 2, base.size)), quarters], axis=-1)
+    pattern = np.take_along_axis(pattern, rng.permuted(np.tile(np.arange(128), (t_n, h_n, 2, 1)), axis=-1), axis=-1)
+    offset = rng.choice([0.0, -8.0, 3.5, -0.25, 6.0], size=(t_n, h_n, 2, 1))
+    e = rng.integers(-3, 4, size=(t_n, h_n, 2, 1)).astype(np.float64)
+    values = (pattern + offset) * 2.0 ** e
+    bits16 = W.f32_to_bf16_bits(values.astype(np.float32))
+    back = (bits16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(back, values), "pattern values must be exact in bf16"
+    k, v = np.ascontiguousarray(bits16[:, :, 0]), np.ascontiguousarray(bits16[:, :, 1])
+    slots = np.arange(t_n, dtype=np.int64)
+    _say(f"rounding ties INT{bits}: {t_n} tokens x {h_n} heads, Hadamard block 1")
+    got = H.download_cache(_gpu_append(k, v, slots, 2, h_n, bits, 1, 0))
+    ref = O.PagedCache(2, h_n, 16, 128, bits)
+    O.append(ref, k, v, slots, 1, 0)
+    gk, gv = H.cache_codes(got)
+    rk, rv = H.cache_codes(ref)
+    want = np.rint(pattern).astype(np.uint8)                      # numpy rounds half to even
+    assert np.all(want[np.isin(pattern, ties)] % 2 == 0)
+    for name, g, r, j in (("K", gk, rk, 0), ("V", gv, rv, 1)):
+        g = g.transpose(0, 2, 1, 3).reshape(t_n, h_n, 128)         # [P, H, ps, D] -> [T, H, D]
+        r = r.transpose(0, 2, 1, 3).reshape(t_n, h_n, 128)
+        assert np.array_equal(r, want[:, :, j]), f"oracle {name} codes differ from the closed form"
+        assert np.array_equal(g, want[:, :, j]), f"GPU {name} codes differ from the closed form"
+    for sz, j in ((got.k_sz, 0), (got.v_sz, 1)):
+        s = sz.transpose(0, 2, 1, 3).reshape(t_n, h_n, 2)
+        assert np.array_equal(s[..., 0].astype(np.float64), (2.0 ** e[:, :, j, 0])), "scale is not 2^e"
+        assert np.array_equal(s[..., 1].astype(np.float64), offset[:, :, j, 0] * 2.0 ** e[:, :, j, 0]), "zero is not o 2^e"
