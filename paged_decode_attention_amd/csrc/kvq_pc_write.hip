@@ -111,20 +111,8 @@ __device__ __forceinline__ void pc_quantize_tile(v4f (&y)[8], bool odd_lb, int c
     for (int i = 0; i < 4; ++i) {
       float cd[8];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) cd[n] = rintf(div_rn(y[n][i] - mn[n], delta[n], r[n]));
-      uint32_t p = 0;
-      if constexpr (BITS == 4) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) p = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(cd[2 * m + 1], 16.0f, cd[2 * m]), m, p);
-      } else {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float bv = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(cd[4 * m + 3], 4.0f, cd[4 * m + 2]), 4.0f,
-                                                         cd[4 * m + 1]), 4.0f, cd[4 * m]);
-          p = __builtin_amdgcn_cvt_pk_u8_f32(bv, m, p);
-        }
-      }
-      packed[i] = p;
+      for (int n = 0; n < 8; ++n) cd[n] = div_rn(y[n][i] - mn[n], delta[n], r[n]);
+      packed[i] = pack_codes<BITS>(cd);
     }
   } else {
     // guarded path: IEEE division, the clamp, zero codes for a constant channel
