@@ -493,6 +493,36 @@ def pin_multi_query_attention():
         assert np.allclose(out[0, :, h], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max()), h
 
 
+def pin_prerotated_query():
+    """A query given already rotated (q_prerotated = 1) attends exactly like the plain query that
+    rotates to it: decode(R q, 1) = decode(q, 0), and the same for multi-query attention. The
+    rotated query y has small integer entries and q = R y is built with scipy's Hadamard matrix
+    (b = 16: R = H_16 / 4), so both y and q are exact in bf16 and neither side of the check uses the
+    oracle's own rotation."""
+    import scipy.linalg
+    b = 16
+    shape = _small_shape(hq=4, hkv=2, b=b, lens=(40, 19, 7))
+    plan = W.plan_pages(shape, 0)
+    cache = _filled_cache(shape, plan)[0]
+    lens = np.array(shape.context_lens)
+    rng = np.random.default_rng(41)
+    blk = scipy.linalg.hadamard(b).astype(np.float64) / 4.0
+    r = np.kron(np.eye(128 // b), blk)
+    y = rng.integers(-2, 3, size=(3, 2, 4, 128)).astype(np.float64)   # rotated queries
+    q = y @ r.T                                                         # q = R y (R symmetric)
+    assert np.array_equal(W.bf16_bits_to_f32(_bits(q)).astype(np.float64), q)   # exact in bf16
+    y_bits, q_bits = _bits(y), _bits(q)
+    plain = O.decode(cache, q_bits[:, 0], plan.block_table, lens, 2, b)
+    pre = O.decode(cache, y_bits[:, 0], plan.block_table, lens, 2, b, q_prerotated=1)
+    assert np.allclose(pre, plain, rtol=1e-6, atol=1e-6 * np.abs(plain).max())
+    # the flag matters: the rotated query taken as a plain one is a different query
+    assert not np.allclose(O.decode(cache, y_bits[:, 0], plan.block_table, lens, 2, b), plain, rtol=1e-3)
+    q_lens = np.array([2, 1, 2])
+    plain = O.multi_query_attention(cache, q_bits, q_lens, plan.block_table, lens, 2, b)
+    pre = O.multi_query_attention(cache, y_bits, q_lens, plan.block_table, lens, 2, b, q_prerotated=1)
+    assert np.allclose(pre, plain, rtol=1e-6, atol=1e-6 * np.abs(plain).max())
+
+
 # ----------------------------------------------------------------------------- bf16 baseline
 
 def pin_bf16_cache_layout():

@@ -246,10 +246,28 @@ def m_pc_v_token_major(mp):
     mp.setattr(O.PagedCachePC, "write_page", write_page)
 
 
+def m_prerotated_rotated_again(mp):
+    # the pre-rotated query is rotated once more (the flag ignored) in decode and multi-query attention
+    real_dec, real_mq = O.decode, O.multi_query_attention
+
+    def dec(cache, q_bits, block_table, context_lens, num_kv_heads, hadamard_block, softmax_scale=0.0,
+            q_prerotated=0, heads=None):
+        return real_dec(cache, q_bits, block_table, context_lens, num_kv_heads, hadamard_block, softmax_scale, 0,
+                        heads)
+
+    def mq(cache, q_bits, q_lens, block_table, context_lens, num_kv_heads, hadamard_block, softmax_scale=0.0,
+           q_prerotated=0, rows=None):
+        return real_mq(cache, q_bits, q_lens, block_table, context_lens, num_kv_heads, hadamard_block, softmax_scale,
+                       0, rows)
+    mp.setattr(O, "decode", dec)
+    mp.setattr(O, "multi_query_attention", mq)
+
+
 MUTATIONS = [m_hadamard_sign, m_hadamard_row_order, m_rotation_norm, m_round_half_up, m_qmax_off_by_one,
              m_zero_is_max, m_pack_high_first, m_v_interleave_swapped, m_no_softmax_scale,
              m_no_inverse_rotation, m_gqa_modulo, m_gather_wrong_offset, m_rms_no_sqrt, m_rms_max_abs, m_bf16_v_token_major, m_bf16_gqa_modulo, m_mq_off_by_one,
-             m_pc_token_axis, m_pc_no_token_scale, m_pc_dequant_without_s, m_pc_tail_off_by_one, m_pc_v_token_major]
+             m_pc_token_axis, m_pc_no_token_scale, m_pc_dequant_without_s, m_pc_tail_off_by_one, m_pc_v_token_major,
+             m_prerotated_rotated_again]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
