@@ -43,6 +43,8 @@
  *     (about a billion token-heads), 2^26 or more (split, sequence, KV head) waves in a decode
  *     (splits of one sequence times sequences times KV heads), or 2^26 or more (query row, head)
  *     pairs in one attention call.
+ *   - An attention call whose max_context_len needs a page (> 0) with num_pages == 0 returns
+ *     KVQ_ERR_SHAPE: the page table would have nothing to point into.
  *   - Alignment (KVQ_ERR_SHAPE otherwise): k, v, q, out, k_codes and v_codes 16 bytes (the
  *     codes argument of kvq_dequant_page 4); slot_mapping, k_sz, v_sz 8; block_table and
  *     context_lens 4; token strides a multiple of 8 elements.
@@ -79,7 +81,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef int32_t kvq_status;
 enum {
@@ -124,9 +126,9 @@ kvq_status kvq_rotate_quantize_append(
     hipStream_t stream);
 
 /*
- * Bytes of device workspace kvq_paged_decode_attention needs for these sizes (0 when the
- * call runs unsplit). pages_per_split: 0 = the library's choice, else the number of pages
- * each split covers. Pass the same values to both calls.
+ * Bytes of device workspace kvq_paged_decode_attention (and kvq_decode_step) needs for these
+ * sizes (0 when the call runs unsplit). pages_per_split: 0 = the library's choice, else the
+ * number of pages each split covers. Pass the same values to both calls.
  */
 size_t kvq_paged_decode_workspace_size(
     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -240,9 +242,10 @@ kvq_status kvq_dequant_page(
  * Baseline (for measurements side by side with the low-bit path): an unquantized bf16 paged
  * cache and split decode attention over it - the kind of BF16 split decode (FlashDecoding-v2,
  * named in the OScaR abstract on the thelatestinai.com page) the pages compare their speed-ups
- * against. Same block table, context lengths, GQA rule, softmax scale, workspace (size from
- * kvq_paged_decode_workspace_size with the same arguments) and error behaviour as
- * kvq_paged_decode_attention; no rotation.
+ * against. Same block table, context lengths, GQA rule, softmax scale and error behaviour as
+ * kvq_paged_decode_attention; no rotation. Its workspace (size from
+ * kvq_paged_decode_bf16_workspace_size with the same arguments) holds only split partials, so
+ * its contents on entry do not matter.
  *
  * Cache layout (bf16 bit patterns, caller-owned device memory):
  *   k_cache  uint16 [num_pages][num_kv_heads][page_size][head_dim]            token-major rows
@@ -257,6 +260,11 @@ kvq_status kvq_bf16_cache_write(
     int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
     const int64_t* slot_mapping, uint16_t* k_cache, uint16_t* v_cache,
     int32_t num_pages, int32_t page_size, hipStream_t stream);
+
+/* Bytes of workspace kvq_paged_decode_attention_bf16 needs (0 when it runs unsplit). */
+size_t kvq_paged_decode_bf16_workspace_size(
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t max_context_len, int32_t page_size, int32_t pages_per_split);
 
 /* Decode attention over the bf16 cache: out float32 [batch][num_q_heads][head_dim];
  * at most 16 query heads per KV head. */

@@ -202,6 +202,16 @@ size_t kvq_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32
   return workspace_layout(p.num_splits, batch, num_q_heads).total;
 }
 
+size_t kvq_paged_decode_bf16_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t max_context_len, int32_t page_size,
+                                            int32_t pages_per_split) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kvq::kHeadDim || page_size <= 0 ||
+      max_context_len < 0 || pages_per_split < 0)
+    return 0;
+  const kvq::SplitPlan p = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
+  return workspace_layout(p.num_splits, batch, num_q_heads).total;
+}
+
 }  // extern "C"
 
 namespace {
@@ -229,6 +239,8 @@ kvq_status decode_args(
     return KVQ_ERR_UNSUPPORTED;
   const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
+  // a page table with entries to read needs a pool to point into
+  if (need_pages > 0 && num_pages == 0) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
   const kvq::SplitPlan plan =
       kvq::plan_splits(batch * tiles, num_kv_heads, max_context_len, page_size, pages_per_split, q_len_max == 0);
@@ -454,6 +466,7 @@ kvq_status kvq_paged_decode_attention_bf16(
   if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
   const int64_t need_pages = (static_cast<int64_t>(max_context_len) + page_size - 1) / page_size;
   if (max_pages_per_seq < need_pages) return KVQ_ERR_SHAPE;
+  if (need_pages > 0 && num_pages == 0) return KVQ_ERR_SHAPE;  // nothing for the page table to point into
   if (batch == 0) return KVQ_OK;
   const kvq::SplitPlan plan = kvq::plan_splits(batch, num_kv_heads, max_context_len, page_size, pages_per_split, true);
   if (!grid_fits(plan.num_splits, 64) || !grid_fits(static_cast<int64_t>(batch) * num_q_heads, 64))
@@ -575,6 +588,8 @@ kvq_status kvq_pc_decode_attention(
   if (num_q_heads / num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
   if (num_kv_heads > 65535 || batch > 65535) return KVQ_ERR_UNSUPPORTED;
   if (max_pages_per_seq < max_context_len / page_size) return KVQ_ERR_SHAPE;
+  // complete pages to read need a pool to point into
+  if (max_context_len / page_size > 0 && num_pages == 0) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
   const kvq::SplitPlan plan = pc_plan(batch, num_kv_heads, max_context_len, page_size, pages_per_split);
   // one wave per page split plus the tail's, and per merged (sequence, head) pair

@@ -21,7 +21,7 @@ EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
            "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page",
            "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step",
            "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention", "kvq_pc_write_pages",
-           "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention")
+           "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention", "kvq_paged_decode_bf16_workspace_size")
 
 
 class KVQError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         _i32, _f32, _p, _p, _sz, _i32, _p]
     L.kvq_bf16_cache_write.restype = _i32
     L.kvq_bf16_cache_write.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _i32, _i32, _p]
+    L.kvq_paged_decode_bf16_workspace_size.restype = _sz
+    L.kvq_paged_decode_bf16_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     L.kvq_paged_decode_attention_bf16.restype = _i32
     L.kvq_paged_decode_attention_bf16.argtypes = [
         _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz, _i32, _p]
@@ -105,6 +107,17 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _own_workspace(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace allocated for one call on ``stream``: the allocation is made with
+    that stream current, so the caching allocator does not hand its memory to another stream's
+    work while the call's kernels may still use it."""
+    if stream is None:
+        return decode_workspace(nbytes, device)
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return decode_workspace(nbytes, device)
 
 
 def _dev(t: torch.Tensor, name: str, dtype) -> int:
@@ -208,6 +221,12 @@ def decode_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def decode_bf16_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
+                               page_size: int, pages_per_split: int = 0) -> int:
+    return int(lib().kvq_paged_decode_bf16_workspace_size(batch, num_q_heads, num_kv_heads, HEAD_DIM,
+                                                            max_context_len, page_size, pages_per_split))
+
+
 def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
                            context_lens: torch.Tensor, max_context_len: int, hadamard_block: int,
                            softmax_scale: float = 0.0, q_prerotated: int = 0, out: torch.Tensor | None = None,
@@ -228,7 +247,7 @@ def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: to
         raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = _own_workspace(need, q.device, stream)
     ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_decode_attention(
         _dev(q, "q", torch.bfloat16), q_prerotated,
@@ -271,7 +290,7 @@ def paged_prefill_attention(q: torch.Tensor, q_lens: torch.Tensor, cache: PagedK
     need = prefill_workspace_size(bsz, qmax, hq, cache.num_kv_heads, max_context_len, cache.page_size,
                                   pages_per_split)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = _own_workspace(need, q.device, stream)
     ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_prefill_attention(
         _dev(q, "q", torch.bfloat16), q_prerotated, _dev(q_lens, "q_lens", torch.int32), qmax,
@@ -310,7 +329,7 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache
         raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
     need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = _own_workspace(need, q.device, stream)
     ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_decode_step(
         _dev(q, "q", torch.bfloat16), q_prerotated, _dev(k_new, "k_new", torch.bfloat16),
@@ -410,9 +429,10 @@ def paged_decode_attention_bf16(q: torch.Tensor, cache: PagedKVCacheBF16, block_
         out = torch.empty((bsz, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     elif tuple(out.shape) != (bsz, hq, HEAD_DIM) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
-    need = decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size, pages_per_split)
+    need = decode_bf16_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len, cache.page_size,
+                                      pages_per_split)
     if workspace is None and need > 0:
-        workspace = decode_workspace(need, q.device)
+        workspace = _own_workspace(need, q.device, stream)
     ws_ptr, ws_bytes = _workspace(workspace)
     st = lib().kvq_paged_decode_attention_bf16(
         _dev(q, "q", torch.bfloat16), _dev(cache.k, "k_cache", torch.bfloat16), _dev(cache.v, "v_cache", torch.bfloat16),
@@ -525,8 +545,8 @@ def pc_decode_attention(q: torch.Tensor, cache: PagedKVCachePC, block_table: tor
     elif tuple(out.shape) != (bsz, hq, HEAD_DIM) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
     if workspace is None:
-        workspace = decode_workspace(pc_decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len,
-                                                              cache.page_size, pages_per_split), q.device)
+        workspace = _own_workspace(pc_decode_workspace_size(bsz, hq, cache.num_kv_heads, max_context_len,
+                                                            cache.page_size, pages_per_split), q.device, stream)
     st = lib().kvq_pc_decode_attention(
         _dev(q, "q", torch.bfloat16), _dev(cache.k_codes, "k_codes", torch.uint8),
         _dev(cache.v_codes, "v_codes", torch.uint8), _dev(cache.k_s, "k_s", torch.float32),

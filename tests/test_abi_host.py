@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(kvq.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert kvq.abi_version() == 1
+    assert kvq.abi_version() == 2
 
 
 def test_status_strings():
@@ -78,6 +78,10 @@ def _decode(**kw):
 def test_decode_validation():
     assert _decode(b=0) == kvq.KVQ_OK
     assert _decode() == kvq.KVQ_ERR_NULL
+    # a context that needs pages with an empty pool is refused before any launch; with no context
+    # to read, an empty pool is fine
+    assert _decode(pages=0) == kvq.KVQ_ERR_SHAPE
+    assert _decode(pages=0, mcl=0) == kvq.KVQ_ERR_NULL
     assert _decode(hq=30) == kvq.KVQ_ERR_SHAPE              # not a multiple of kv heads
     assert _decode(hq=72) == kvq.KVQ_ERR_UNSUPPORTED        # 9 query heads per kv head
     assert _decode(bits=1) == kvq.KVQ_ERR_UNSUPPORTED
@@ -101,6 +105,9 @@ def test_workspace_size():
     assert w8 >= 8 * 32 * 130 * 4
     assert L.kvq_paged_decode_workspace_size(1, 32, 8, 128, 8192, 16, 512) == 0   # one split
     assert L.kvq_paged_decode_workspace_size(0, 32, 8, 128, 8192, 16, 0) == 0
+    # the bf16 baseline's split partials: 8 splits x 32 rows of 128 floats and (max, sum) pairs
+    assert L.kvq_paged_decode_bf16_workspace_size(1, 32, 8, 128, 8192, 16, 64) == 8 * 32 * 128 * 4 + 8 * 32 * 8
+    assert L.kvq_paged_decode_bf16_workspace_size(1, 32, 8, 128, 8192, 16, 512) == 0
 
 
 def _splits(batch, hq, hkv, max_len, pps=0):
@@ -167,9 +174,11 @@ def test_bf16_baseline_validation():
 
     def dec(**kw):
         return L.kvq_paged_decode_attention_bf16(
-            NULL, NULL, NULL, 10, 16, NULL, kw.get("mp", 4), NULL, kw.get("ml", 64), kw.get("b", 2),
+            NULL, NULL, NULL, kw.get("pages", 10), 16, NULL, kw.get("mp", 4), NULL, kw.get("ml", 64), kw.get("b", 2),
             kw.get("hq", 32), kw.get("hkv", 8), 128, 0.0, NULL, NULL, 0, 0, NULL)
     assert dec() == kvq.KVQ_ERR_NULL
+    assert dec(pages=0) == kvq.KVQ_ERR_SHAPE          # pages to read, an empty pool
+    assert dec(pages=0, ml=0) == kvq.KVQ_ERR_NULL
     assert dec(b=0) == kvq.KVQ_OK
     assert dec(hq=30) == kvq.KVQ_ERR_SHAPE            # not a multiple of the KV heads
     assert dec(hq=136) == kvq.KVQ_ERR_UNSUPPORTED     # 17 query heads per KV head
@@ -231,6 +240,8 @@ def _pc_decode(**kw):
 
 
 def test_pc_validation_and_workspace():
+    assert _pc_decode(pages=0) == kvq.KVQ_ERR_SHAPE       # complete pages to read, an empty pool
+    assert _pc_decode(pages=0, mcl=63) == kvq.KVQ_ERR_NULL  # only the unfinished page (the tail)
     assert _pc_write(n=0) == kvq.KVQ_OK
     assert _pc_write() == kvq.KVQ_ERR_NULL
     assert _pc_write(n=-1) == kvq.KVQ_ERR_SHAPE

@@ -40,7 +40,8 @@ def _oracle_cache(shape, lens, plan=None):
 
 def _gpu_decode(shape, plan, dev_cache, q, lens, pps=0):
     max_len = int(max(lens)) if len(lens) else 0
-    nbytes = kvq.decode_workspace_size(len(lens), shape.num_q_heads, shape.num_kv_heads, max_len, shape.page_size, pps)
+    nbytes = kvq.decode_bf16_workspace_size(len(lens), shape.num_q_heads, shape.num_kv_heads, max_len,
+                                            shape.page_size, pps)
     ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")   # contents must not matter
     out = kvq.paged_decode_attention_bf16(H.to_dev_bf16(q), dev_cache, H.to_dev(plan.block_table),
                                           H.to_dev(np.asarray(lens, dtype=np.int32)), max_len, workspace=ws,
