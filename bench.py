@@ -42,6 +42,10 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="llama3_8b")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", choices=("tiny", "sweep", "llama2_70b", "oscar_int2"),
+                   help="time only this record (with its measured ceilings, without the CPU oracle) and print it")
+    p.add_argument("--no-sub-records", action="store_true",
+                   help="time only the Llama-3-8B step (no tiny, sweep, Llama-2-70B and OScaR records, no ceilings)")
     p.add_argument("--decode-iters", type=int, default=200, help="extra decode-only launches for the decode roofline")
     p.add_argument("--counters", action="store_true",
                    help="short program for rocprofv3 --pmc passes: a 256 MiB calibration copy, then --steps steps")
@@ -277,6 +281,401 @@ def cpu_baseline(shape, k, v, slots, plan, q) -> dict:
         "append_GBps": round(ab / (t1 - t0) / 1e9, 4), "decode_GBps": round(db / (t2 - t1) / 1e9, 4),
         "decode_tokens_per_s": round(n_seq / (t2 - t1), 3),
     }
+
+
+# ----------------------------------------------------------------------------- measured ceiling
+
+class Ceiling:
+    """Streaming probes (libkvq_stream.so) at a kernel's launch shape: how fast HBM serves a launch of
+    the same grid, workgroup size and bytes that only moves bytes (16-byte non-temporal loads,
+    16-byte stores, linear). Launches rotate over 1.5 GiB pools, so the 256 MB last-level cache
+    cannot serve them. The paged kernels' reads are scattered page by page; the probe's linear
+    stream is an upper bound for them."""
+    POOL = 1536 << 20
+
+    def __init__(self, dev):
+        import torch
+        from paged_decode_attention_amd import stream_probe
+        self.sp = stream_probe
+        self.src = torch.ones(self.POOL, dtype=torch.uint8, device=dev)
+        self.dst = torch.zeros(self.POOL, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def measure(self, name, read_bytes, write_bytes, read_units, write_units, grid, block, stream, n_blocks=6,
+                per_block=10, layout=0):
+        """GB/s of (read + write) bytes per launch, median over blocks of ``per_block`` launches."""
+        import torch
+        rows = max(-(-read_bytes // (16 * read_units)) if read_units else 0,
+                   -(-write_bytes // (16 * write_units)) if write_units else 0)
+        rb, wb = rows * read_units * 16, rows * write_units * 16
+        step_r, step_w = -(-rb // (1 << 20)) << 20, -(-wb // (1 << 20)) << 20
+
+        def launch(i):
+            so = (i * step_r) % max(1, self.POOL - rb) // 4096 * 4096 if rb else 0
+            do = (i * step_w) % max(1, self.POOL - wb) // 4096 * 4096 if wb else 0
+            self.sp.probe(self.src, self.dst, rows, read_units, write_units, grid, block, self.sink, stream, so, do,
+                          layout=layout)
+        for i in range(5):
+            launch(i)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_blocks)]
+        for j in range(n_blocks):
+            evs[j][0].record(stream)
+            for i in range(per_block):
+                launch(5 + j * per_block + i)
+            evs[j][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([e[0].elapsed_time(e[1]) / per_block for e in evs])
+        med = float(np.median(ms))
+        lay = (("reads and writes in every wave", "reader and writer workgroups")[layout]
+               if read_units and write_units else "one linear stream")
+        return {"pattern": name, "layout": lay,
+                "GBps": round((rb + wb) / med / 1e6, 1), "read_bytes": rb, "write_bytes": wb,
+                "grid": grid, "block": block, "median_us": round(med * 1e3, 2),
+                "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2)}
+
+    def for_decode(self, nbytes, waves, stream):
+        """A decode launch: one 64-lane workgroup per split wave, reading ``nbytes``."""
+        return self.measure("read-only, non-temporal", nbytes, 0, 32, 0, waves, 64, stream)
+
+    def for_append(self, token_heads, bits, stream, patterns=("mix",)):
+        """An append launch (one wave per 16-token item, four per 256-thread workgroup) moving the
+        append's bytes: 512 read and 2 (128 bits / 8) + 16 written per token-head."""
+        items = -(-token_heads // 16)  # (16-token tile, KV head) items
+        grid = -(-items // 4)
+        wr = 2 * 128 * bits // 8 + 16
+        rd = 512
+        out = {}
+        total = token_heads * (rd + wr)
+        if "mix" in patterns:
+            # both layouts; the faster one is the ceiling
+            name = f"read/write mix {rd}:{wr} ({100 * rd / (rd + wr):.0f}/{100 * wr / (rd + wr):.0f})"
+            tries = [self.measure(name, token_heads * rd, token_heads * wr, rd // 16, wr // 16, grid, 256, stream,
+                                  layout=lay) for lay in (0, 1)]
+            out["mix"] = max(tries, key=lambda t: t["GBps"])
+            out["mix_other_layout"] = min(tries, key=lambda t: t["GBps"])
+        if "read" in patterns:
+            out["read"] = self.measure("read-only, non-temporal", total, 0, 32, 0, grid, 256, stream)
+        if "write" in patterns:
+            out["write"] = self.measure("write-only", 0, total, 0, 32, grid, 256, stream)
+        if "copy" in patterns:
+            tries = [self.measure("copy (half read, half written)", total // 2, total // 2, 16, 16, grid, 256, stream,
+                                  layout=lay) for lay in (0, 1)]
+            out["copy"] = max(tries, key=lambda t: t["GBps"])
+        return out
+
+
+def _decode_waves(batch, num_q_heads, num_kv_heads, max_len, page_size):
+    """Waves of the one-query decode launch: splits (read back from the workspace size, which holds
+    a (128 + 2)-float row per split, sequence and query head) times sequences times KV heads."""
+    from paged_decode_attention_amd import kvq
+    w = kvq.decode_workspace_size(batch, num_q_heads, num_kv_heads, max_len, page_size)
+    splits = round(w / (batch * num_q_heads * (128 * 4 + 8))) if w else 1
+    return splits * batch * num_kv_heads
+
+
+def _pcts(ms):
+    ms = np.asarray(ms)
+    return {"median_ms": round(float(np.median(ms)), 5), "p10_ms": round(float(np.percentile(ms, 10)), 5),
+            "p90_ms": round(float(np.percentile(ms, 90)), 5)}
+
+
+def _roofline(kernel, nbytes, ms, ceiling_gbps, traffic):
+    gb = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gb / PEAK_HBM_GBPS, 4),
+            "frac_of_measured_ceiling": round(gb / ceiling_gbps, 4) if ceiling_gbps else None,
+            "measured_ceiling": ceiling_gbps, "traffic": traffic, "kernel": kernel, "bytes_per_launch": nbytes}
+
+
+def _say(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _block_times(fn, n_blocks, per_block, stream, start=0):
+    """Per-call ms of fn over n_blocks event-bracketed blocks of per_block back-to-back calls."""
+    import torch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_blocks)]
+    for j in range(n_blocks):
+        evs[j][0].record(stream)
+        for i in range(per_block):
+            fn(start + j * per_block + i)
+        evs[j][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([e[0].elapsed_time(e[1]) / per_block for e in evs])
+
+
+def record_llama2_70b(dev, stream, ceiling):
+    """The Llama-2-70B-shaped step: 80 independent layer caches (4 x 32768 tokens, 64/8 heads, INT4);
+    per layer one fused decode step (append of each sequence's new token + attention over 32769
+    tokens + split merge). Returns the record and the layer-0 decode-step closures' inputs."""
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("llama2_70b")
+    layers = []
+    for l in range(shape.layers):
+        plan = W.plan_pages(shape, extra_tokens=1, layer=l)
+        caches = _filled_caches(shape, plan, 1, dev, stream, layer=l)
+        layers.append(_decode_step_fns(shape, plan, caches, dev, stream, layer=l))
+    _say(f"{shape.name}: {shape.layers} layer caches filled")
+
+    def step(i):
+        for append, _, _ in layers:
+            append.fused(0)
+
+    def attention(i):
+        for _, attend, _ in layers:
+            attend(0)
+    for i in range(3):
+        step(i)
+        attention(i)
+    torch_sync()
+    steps = _block_times(step, 8, 1, stream)
+    att = _block_times(attention, 4, 1, stream)
+    lens = layers[0][2]
+    b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+    b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits)
+    per_layer = steps / shape.layers
+    t_layer = float(np.mean(per_layer))
+    waves = _decode_waves(shape.batch, shape.num_q_heads, shape.num_kv_heads, int(np.max(lens)), shape.page_size)
+    del layers, step, attention
+    torch_empty_cache()
+    ceil = ceiling.for_decode(b_att, waves, stream)
+    t_dec = [stored_traffic(shape.name, k) for k in ("decode_mfma_kernel", "decode_merge_splits_kernel")]
+    t_dec = None if None in t_dec else sum(t_dec)
+    step_ms = float(np.mean(steps))
+    rec = {
+        "workload": "llama2_70b: 4 seq x 32768 tokens, 64/8 heads, head_dim 128, page 16, Hadamard block 128, INT4, "
+                    "80 independent layer caches; one step = per layer a fused decode step (append of the new token "
+                    "+ attention over 32769 tokens + split merge)",
+        "layers": shape.layers, "step_ms": round(step_ms, 4), "step": _pcts(steps),
+        "tokens_per_s": round(shape.batch / (step_ms * 1e-3), 1),
+        "step_GBps": round((b_att + b_app) * shape.layers / (step_ms * 1e-3) / 1e9, 1),
+        "decode_step_per_layer_ms": round(t_layer, 5),
+        "attention_only_per_layer_ms": round(float(np.mean(att)) / shape.layers, 5),
+        "roofline": _roofline("kvq_decode_step, one layer (decode + split merge launches)", b_att + b_app, t_layer,
+                              ceil["GBps"], t_dec),
+        "ceiling_decode_shape": ceil,
+    }
+    return rec
+
+
+def record_oscar(dev, stream, ceiling):
+    """The OScaR INT2 shape (32 x 16384 tokens, 28/4 heads, rotation + per-token scaling + INT2):
+    512-token chunk appends that land mid-page, then decode attention over 16385 tokens."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("oscar_int2")
+    plan = W.plan_pages(shape, extra_tokens=1)
+    calls = W.chunk_schedule(shape)
+    n_tok = sum(len(sq) for sq, _ in calls)
+    k, v = W.draw_kv_device(shape, n_tok, dev)
+    cache = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+    slot_list, offs, o = [], [], 0
+    for sq, ps in calls:
+        slot_list.append(torch.from_numpy(W.slots_for_positions(plan, shape.page_size, sq, ps)).to(dev))
+        offs.append((o, o + len(sq)))
+        o += len(sq)
+    full = [i for i, (a, b) in enumerate(offs) if b - a == shape.batch * shape.chunk]
+    for i, ((a, b), sl) in enumerate(zip(offs, slot_list)):
+        if i not in full:
+            kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale,
+                                       stream=stream)
+
+    def chunk(i):
+        (a, b), sl = offs[full[i % len(full)]], slot_list[full[i % len(full)]]
+        kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale, stream=stream)
+    # the chunks in order, each timed on its own (one event pair per chunk): the serving loop's calls
+    chunk_ms = _block_times(chunk, len(full), 1, stream)
+    del k, v
+    copies = [cache] + [kvq.PagedKVCache(cache.k_codes.clone(), cache.v_codes.clone(), cache.k_sz.clone(),
+                                         cache.v_sz.clone(), cache.bits) for _ in range(7)]
+    append, attend, lens = _decode_step_fns(shape, plan, copies, dev, stream)
+    for i in range(5):
+        attend(i)
+        append.fused(i)
+    att = _block_times(attend, 6, 10, stream)
+    fused = _block_times(append.fused, 6, 10, stream)
+    b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+    b_chunk = append_bytes(shape.batch * shape.chunk, shape.num_kv_heads, shape.bits)
+    b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits)
+    waves = _decode_waves(shape.batch, shape.num_q_heads, shape.num_kv_heads, int(np.max(lens)), shape.page_size)
+    del copies, cache, append, attend
+    torch_empty_cache()
+    t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream)
+    torch_empty_cache()
+    c_dec = ceiling.for_decode(b_att, waves, stream)
+    c_app = ceiling.for_append(shape.batch * shape.chunk * shape.num_kv_heads, shape.bits, stream)["mix"]
+    t_dec = [stored_traffic(shape.name, kk) for kk in ("decode_mfma_kernel", "decode_merge_splits_kernel")]
+    t_dec = None if None in t_dec else sum(t_dec)
+    t_ms = float(np.mean(att))
+    c_ms = float(np.mean(chunk_ms))
+    f_ms = float(np.mean(fused))
+    return {
+        "workload": "oscar_int2: 32 seq x 16384 tokens, 28/4 heads, head_dim 128, page 16, Hadamard block 128, "
+                    "per-token scaling, INT2; 512-token chunk appends landing mid-page, then decode attention over "
+                    "16385 tokens",
+        "attention": _pcts(att), "decode_tokens_per_s": round(shape.batch / (t_ms * 1e-3), 1),
+        "fused_decode_step": _pcts(fused), "fused_tokens_per_s": round(shape.batch / (f_ms * 1e-3), 1),
+        "fused_decode_step_GBps": round((b_att + b_app) / (f_ms * 1e-3) / 1e9, 1),
+        "chunk_append": dict(_pcts(chunk_ms), chunks=len(full), bytes=b_chunk,
+                             tokens_per_s=round(shape.batch * shape.chunk / (c_ms * 1e-3), 1)),
+        "roofline": _roofline("kvq_paged_decode_attention (decode + split merge launches)", b_att, t_ms,
+                              c_dec["GBps"], t_dec),
+        "roofline_chunk_append": _roofline("kvq_rotate_quantize_append, 32 x 512-token chunk", b_chunk, c_ms,
+                                           c_app["GBps"], stored_traffic(shape.name, "append_kernel")),
+        "ceiling_decode_shape": c_dec, "ceiling_chunk_append_shape": c_app,
+        "baseline_bf16_decode": {"avg_ms": round(t_bf, 5), "GBps": round(gb_bf, 1),
+                                 "speedup_of_int2_decode": round(t_bf / t_ms, 2),
+                                 "cache_bytes_ratio": round(512 / (2 * 128 * shape.bits // 8 + 16), 2)},
+    }
+
+
+def record_sweep(dev, stream):
+    """The concurrency sweep on the Llama-3-8B layer shape: batch 1 ... 256, ragged contexts
+    U{512..8192}, Hadamard block 64; one fused decode step (append + attention) per batch size."""
+    from paged_decode_attention_amd import workloads as W
+    rows = []
+    for b in (1, 8, 32, 128, 256):
+        shape = W.config(f"sweep_b{b}")
+        plan = W.plan_pages(shape, extra_tokens=1)
+        n_copies = int(min(32, max(1, math.ceil(1.1e9 / _cache_bytes(shape, plan.num_pages)))))
+        caches = _filled_caches(shape, plan, n_copies, dev, stream)
+        append, attend, lens = _decode_step_fns(shape, plan, caches, dev, stream)
+        for i in range(5):
+            append.fused(i)
+            attend(i)
+        fused = _block_times(append.fused, 5, 10, stream)
+        att = _block_times(attend, 5, 10, stream)
+        b_att = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
+        b_app = append_bytes(shape.batch, shape.num_kv_heads, shape.bits)
+        f_ms, a_ms = float(np.mean(fused)), float(np.mean(att))
+        rows.append({"batch": b, "tokens": int(np.sum(lens)), "fused_decode_step": _pcts(fused),
+                     "tokens_per_s": round(b / (f_ms * 1e-3), 1),
+                     "fused_GBps": round((b_att + b_app) / (f_ms * 1e-3) / 1e9, 1),
+                     "attention": _pcts(att), "attention_GBps": round(b_att / (a_ms * 1e-3) / 1e9, 1)})
+        del caches, append, attend
+        torch_empty_cache()
+    return {"workload": "sweep: Llama-3-8B layer shape, batch 1/8/32/128/256, ragged contexts U{512..8192}, page 16, "
+                        "Hadamard block 64, INT4; one fused decode step per batch (eager launches)",
+            "rows": rows}
+
+
+def record_tiny(dev, stream):
+    """The tiny single-layer check (1 x 512 tokens, 8/8 heads, Hadamard block 32): latency of the
+    prefill append and of the fused decode step, eager launches."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config("tiny")
+    plan = W.plan_pages(shape, extra_tokens=1)
+    seq, pos = W.prefill_order(shape)
+    slots = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, seq, pos)).to(dev)
+    k, v = W.draw_kv_device(shape, len(seq), dev)
+    cache = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+    pre = _block_times(lambda i: kvq.rotate_quantize_append(k, v, slots, cache, shape.hadamard_block, 0,
+                                                            stream=stream), 5, 10, stream)
+    append, _, _ = _decode_step_fns(shape, plan, [cache], dev, stream)
+    fused = _block_times(append.fused, 5, 10, stream)
+    return {"workload": "tiny: 1 seq x 512 tokens, 8/8 heads, head_dim 128, page 16, Hadamard block 32, INT4",
+            "prefill_append": _pcts(pre), "fused_decode_step": _pcts(fused)}
+
+
+def cpu_decode_baseline(name, n_seq, extrapolate=1.0, note=""):
+    """The oracle (as it stands) on the first n_seq sequences of a workload: its append of their
+    prefill (set-up, timed separately) and its decode (one query per head) over the prefill; GB/s of
+    the decode's algorithmic bytes, and tokens/s of the decode scaled to the whole workload by
+    ``extrapolate`` (the sample's share of it)."""
+    from oracle import kvq_oracle as O
+    from paged_decode_attention_amd import workloads as W
+    shape = W.config(name)
+    s = shape.with_(batch=n_seq, context_lens=tuple(shape.context_lens[:n_seq]))
+    plan = W.plan_pages(s, extra_tokens=0)
+    seq, pos = W.prefill_order(s)
+    k, v = W.draw_kv(s, len(seq))
+    cache = O.PagedCache(plan.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.bits)
+    t0 = time.perf_counter()
+    O.append(cache, k, v, W.slots_for_positions(plan, s.page_size, seq, pos), s.hadamard_block, s.token_scale)
+    t1 = time.perf_counter()
+    q = W.draw_q(s)
+    O.decode(cache, q, plan.block_table, np.asarray(s.context_lens), s.num_kv_heads, s.hadamard_block)
+    t2 = time.perf_counter()
+    nb = decode_bytes(np.asarray(s.context_lens), s.num_q_heads, s.num_kv_heads, s.bits, s.page_size)
+    ab = append_bytes(len(seq), s.num_kv_heads, s.bits)
+    out = {"kind": "oracle", "cores": len(os.sched_getaffinity(0)),
+           "sample": f"{name}: append of the prefill of {n_seq} of {shape.batch} sequences ({len(seq)} tokens, "
+                     f"{t1 - t0:.1f} s), then decode of those {n_seq} x {s.num_q_heads} heads ({t2 - t1:.1f} s)" + note,
+           "decode_GBps": round(nb / (t2 - t1) / 1e9, 5), "append_GBps": round(ab / (t1 - t0) / 1e9, 5),
+           "decode_s": round(t2 - t1, 3)}
+    if extrapolate != 1.0:
+        out["extrapolated"] = True
+        out["extrapolated_decode_step_s"] = round((t2 - t1) * extrapolate, 2)
+        out["decode_tokens_per_s"] = round(shape.batch / ((t2 - t1) * extrapolate), 5)
+    else:
+        out["decode_tokens_per_s"] = round(shape.batch / (t2 - t1), 5)
+    return out
+
+
+def counters_other(args, dev):
+    """--counters for the Llama-2-70B and OScaR workloads: set-up, three calibration copies of known
+    size, then the dispatches the counters are read on (no copy after the calibration)."""
+    import torch
+    from paged_decode_attention_amd import kvq
+    from paged_decode_attention_amd import workloads as W
+    stream = torch.cuda.current_stream()
+    shape = W.config(args.workload)
+    if shape.name == "llama2_70b":
+        layers = []
+        for l in range(4):
+            plan = W.plan_pages(shape, extra_tokens=1, layer=l)
+            caches = _filled_caches(shape, plan, 1, dev, stream, layer=l)
+            layers.append(_decode_step_fns(shape, plan, caches, dev, stream, layer=l))
+
+        def run():
+            for i in range(args.steps):
+                for append, _, _ in layers:
+                    append.fused(0)
+        what = f"{args.steps} x 4 layers of fused decode steps"
+    else:
+        plan = W.plan_pages(shape, extra_tokens=1)
+        calls = W.chunk_schedule(shape)
+        n_tok = sum(len(sq) for sq, _ in calls)
+        k, v = W.draw_kv_device(shape, n_tok, dev)
+        cache = kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+        work, o = [], 0
+        for sq, ps in calls:
+            sl = torch.from_numpy(W.slots_for_positions(plan, shape.page_size, sq, ps)).to(dev)
+            work.append((o, o + len(sq), sl))
+            o += len(sq)
+        full = [w for w in work if w[1] - w[0] == shape.batch * shape.chunk]
+        for a, b, sl in work:
+            if b - a != shape.batch * shape.chunk:
+                kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale,
+                                           stream=stream)
+        copies = [kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
+                  for _ in range(4)]
+        _, attend, _ = _decode_step_fns(shape, plan, copies, dev, stream)
+
+        def run():
+            for a, b, sl in full[:args.steps]:
+                kvq.rotate_quantize_append(k[a:b], v[a:b], sl, cache, shape.hadamard_block, shape.token_scale,
+                                           stream=stream)
+            for i in range(args.steps):
+                attend(i)
+        what = f"{min(args.steps, len(full))} chunk appends of 32 x 512 tokens, then {args.steps} decodes"
+    torch.cuda.synchronize()
+    src = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    run()
+    torch.cuda.synchronize()
+    print(f"counters run ({shape.name}): 3 calibration copies of {CALIBRATION_BYTES} bytes, {what}", flush=True)
+
+
+def torch_sync():
+    import torch
+    torch.cuda.synchronize()
 
 
 # ----------------------------------------------------------------------------- workload suite
@@ -780,12 +1179,16 @@ def main():
         print(summarize_sq(*args.summarize_sq, args.workload))
         return
     if args.summarize_kernel_stats:
-        if args.suite_only:  # a trace of suite rows
+        if args.only:  # a trace of one record
+            cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
+                   f"--only {args.only}")
+        elif args.suite_only:  # a trace of suite rows
             cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
                    f"--suite --suite-only {args.suite_only}")
         else:
             cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- python3 bench.py "
-                   f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline")
+                   f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu-baseline"
+                   + (" --no-sub-records" if args.no_sub_records else ""))
         print(summarize_kernel_stats(args.summarize_kernel_stats, cmd))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -806,6 +1209,17 @@ def main():
         sys.exit(1)
     kvq.lib()
     dev = torch.device("cuda:0")
+    if args.counters and args.workload in ("llama2_70b", "oscar_int2"):
+        counters_other(args, dev)
+        return
+    if args.only:
+        stream = torch.cuda.current_stream()
+        if args.only in ("tiny", "sweep"):
+            rec = (record_tiny if args.only == "tiny" else record_sweep)(dev, stream)
+        else:
+            rec = (record_llama2_70b if args.only == "llama2_70b" else record_oscar)(dev, stream, Ceiling(dev))
+        print(json.dumps(rec), flush=True)
+        return
     shape = W.config(args.workload)
     assert shape.layers == 1 and shape.chunk == 0, "the step benchmark covers single-layer prefill workloads"
     plan = W.plan_pages(shape, extra_tokens=1)
@@ -961,7 +1375,8 @@ def main():
                                            "in_step_event_ms": round(float(prefill_ms.mean()), 5),
                                            "GBps": round(gbps(b_prefill, pre_avg), 1),
                                            "frac_of_peak": round(gbps(b_prefill, pre_avg) / PEAK_HBM_GBPS, 4),
-                                           "tokens_per_s": round(len(seq) / (pre_avg * 1e-3), 1)},
+                                           "tokens_per_s": round(len(seq) / (pre_avg * 1e-3), 1),
+                                           **_pcts(prefill_blk_ms)},
         "decode_step_fused_in_step": {"bytes": b_dapp + b_attn, "avg_ms": round(dstep_avg, 5),
                                       "GBps": round(gbps(b_dapp + b_attn, dstep_avg), 1),
                                       "note": "kvq_decode_step: decode-token append + attention in one launch"},
@@ -1008,14 +1423,61 @@ def main():
         "kernels": kernels, "roofline": roofline, "roofline_decode": roofline_decode,
     }
     # the same decode over an unquantized bf16 cache (the baseline the pages compare against)
-    del caches
+    del caches, k_in, v_in
     torch.cuda.empty_cache()
     t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream, n_copies=4)
     result["baseline_bf16_decode"] = {
         "avg_ms": round(t_bf, 5), "GBps": round(gb_bf, 1), "speedup_of_int%d_decode" % shape.bits: round(t_bf / dec_avg, 2),
         "cache_bytes_ratio": round(512 / (2 * 128 * shape.bits // 8 + 16), 2)}
+    torch_empty_cache()
+    _say(f"{shape.name} step timed")
+    if not args.no_sub_records:
+        # the practical ceiling at the two kernels' launch shapes
+        ceiling = Ceiling(dev)
+        c_dec = ceiling.for_decode(b_attn, _decode_waves(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
+                                                         shape.page_size), stream)
+        c_app = ceiling.for_append(len(seq) * shape.num_kv_heads, shape.bits, stream,
+                                   patterns=("mix", "read", "write", "copy"))
+        result["ceiling"] = {"unit": "GB/s", "decode_shape": c_dec, "append_shape": c_app,
+                             "note": "streaming probes (libkvq_stream.so) with the kernels' grid, workgroup size and "
+                                     "bytes, linear 16-byte accesses; the append's ceiling is its read/write mix"}
+        roofline["measured_ceiling"] = c_app["mix"]["GBps"] if dominant.startswith("rotate") else c_dec["GBps"]
+        roofline["frac_of_measured_ceiling"] = round(achieved / roofline["measured_ceiling"], 4)
+        roofline_decode["measured_ceiling"] = c_dec["GBps"]
+        roofline_decode["frac_of_measured_ceiling"] = round(roofline_decode["achieved"] / c_dec["GBps"], 4)
+        _say("ceilings measured")
+        subs = {}
+        subs["tiny"] = record_tiny(dev, stream)
+        subs["sweep"] = record_sweep(dev, stream)
+        _say("sweep timed")
+        subs["llama2_70b"] = record_llama2_70b(dev, stream, ceiling)
+        _say("llama2_70b timed")
+        subs["oscar_int2"] = record_oscar(dev, stream, ceiling)
+        _say("oscar_int2 timed")
+        del ceiling
+        torch_empty_cache()
+        result["sub_records"] = subs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shape, k, v, slots, plan, q)
+        _say(f"{shape.name} CPU oracle timed")
+        if not args.no_sub_records:
+            subs["tiny"]["cpu_baseline"] = cpu_decode_baseline("tiny", 1)
+            for row in subs["sweep"]["rows"]:
+                b = row["batch"]
+                if b in (1, 8):
+                    row["cpu_baseline"] = cpu_decode_baseline(f"sweep_b{b}", b)
+                elif b == 32:
+                    lens32 = W.config("sweep_b32").context_lens
+                    row["cpu_baseline"] = cpu_decode_baseline(
+                        "sweep_b32", 8, extrapolate=sum(lens32) / sum(lens32[:8]),
+                        note="; scaled to all 32 by their tokens")
+            _say("sweep CPU oracle timed")
+            subs["llama2_70b"]["cpu_baseline"] = cpu_decode_baseline(
+                "llama2_70b", 1, extrapolate=4 * 80, note="; one sequence of one layer, x 4 sequences x 80 layers")
+            _say("llama2_70b CPU oracle timed")
+            subs["oscar_int2"]["cpu_baseline"] = cpu_decode_baseline(
+                "oscar_int2", 4, extrapolate=8, note="; 4 of the 32 sequences, x 8")
+            _say("oscar_int2 CPU oracle timed")
     print(json.dumps(result), flush=True)
 
 

@@ -25,6 +25,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
+# the streaming probes that measure the HBM ceiling (measurement support, include/kvq_stream.h)
+STREAM_LIB = os.path.join(PKG, "libkvq_stream.so")
+STREAM_SOURCES = ["kvq_stream.hip"]
 SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_dequant.hip",
            "kvq_baseline_bf16.hip", "kvq_pc.hip", "kvq_pc_write.hip"]
 
@@ -54,18 +57,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {lib}", file=sys.stderr)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + STREAM_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], STREAM_LIB, verbose)
     return LIB
 
 
