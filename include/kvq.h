@@ -171,6 +171,34 @@ kvq_status kvq_paged_decode_attention(
     hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kvq_paged_decode_attention with the split partials in
+ * a fixed scratch array inside the library instead of a caller workspace. Arguments, layouts,
+ * results and error behaviour are those of kvq_paged_decode_attention without workspace and
+ * workspace_bytes; the same kernels run. The call allocates nothing.
+ *
+ * The scratch is KVQ_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB) of device memory per GPU, taken when the
+ * library's code is loaded on that GPU and held until the process ends. Sizes whose partials
+ * (kvq_paged_decode_workspace_size with the same arguments) exceed it return KVQ_ERR_WORKSPACE
+ * before anything is launched. Every call on one GPU shares that GPU's scratch, and its contents
+ * are those of the last call: calls that overlap on one GPU (other streams, other threads) race
+ * and give undefined results; serialize them (e.g. one stream). The first call on a GPU looks up
+ * that GPU's scratch address (a HIP runtime query, no allocation).
+ */
+#define KVQ_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+kvq_status kvq_paged_decode_attention_noalloc(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, int32_t pages_per_split,
+    hipStream_t stream);
+
+/*
  * Several queries per sequence - chunked prefill, speculative verification: the causal attention
  * of each sequence's last q_lens[b] tokens, already appended to the cache, over its context (the
  * paged low-bit attention of the decode, with query tiles of more than one token).

@@ -3,6 +3,7 @@
 // kvq_pc_write.hip and kvq_pc.hip.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/kvq.h"
 #include "kvq_launch.h"
@@ -129,7 +130,7 @@ const char* kvq_status_string(int32_t status) {
     case KVQ_ERR_NULL: return "a required pointer is NULL";
     case KVQ_ERR_SHAPE: return "invalid or inconsistent size, stride, block size or alignment";
     case KVQ_ERR_UNSUPPORTED: return "unsupported configuration (bits must be 2 or 4, head_dim 128, page_size a multiple of 16 (per-channel pages: 32, 64 or 128), at most 8 query heads per KV head for a single query)";
-    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case KVQ_ERR_WORKSPACE: return "decode workspace missing or too small (allocation-free decode: the split partials exceed its fixed scratch)";
     case KVQ_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";
   }
@@ -309,6 +310,71 @@ kvq_status kvq_paged_decode_attention(
                                  pages_per_split))
     return s;
   if (batch == 0) return KVQ_OK;
+  return kvq::launch_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------- allocation-free decode
+//
+// The split partials of kvq_paged_decode_attention_noalloc live in this array: one copy per GPU,
+// placed by the runtime when the library's code is loaded there. Host code never uses its name as
+// an address (on the host it is only a stand-in for the symbol): each GPU's copy is looked up once
+// with hipGetSymbolAddress, with that GPU current, and the kernels take that address.
+static __device__ __align__(256) uint8_t scratch[KVQ_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device (null until looked up)
+
+// The current device's copy of `scratch`.
+kvq_status scratch_address(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_paged_decode_attention_noalloc(
+    const uint16_t* q, int32_t q_prerotated,
+    const uint8_t* k_codes, const uint8_t* v_codes, const float* k_sz, const float* v_sz,
+    int32_t num_pages, int32_t page_size,
+    const int32_t* block_table, int32_t max_pages_per_seq,
+    const int32_t* context_lens, int32_t max_context_len,
+    int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t hadamard_block, int32_t bits, float softmax_scale,
+    float* out, int32_t pages_per_split,
+    hipStream_t stream) {
+  // Validate every argument, and that the partials fit the scratch, against an aligned non-null
+  // stand-in for the scratch's address (never dereferenced): nothing touches the device before
+  // the call is known to be valid.
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t{256});
+  kvq::DecodeArgs a;
+  if (kvq_status s = decode_args(a, q, q_prerotated, k_codes, v_codes, k_sz, v_sz, num_pages, page_size, block_table,
+                                 max_pages_per_seq, context_lens, max_context_len, batch, num_q_heads, num_kv_heads,
+                                 head_dim, hadamard_block, bits, softmax_scale, out, stand_in,
+                                 KVQ_DECODE_NOALLOC_SCRATCH_BYTES, pages_per_split))
+    return s;
+  if (batch == 0) return KVQ_OK;
+  if (a.ws_acc) {  // split: point the partials at this GPU's scratch, at the same offsets
+    char* base = nullptr;
+    if (kvq_status s = scratch_address(&base)) return s;
+    const char* const si = static_cast<const char*>(stand_in);
+    a.ws_acc = reinterpret_cast<float*>(base + (reinterpret_cast<const char*>(a.ws_acc) - si));
+    a.ws_ml = reinterpret_cast<float*>(base + (reinterpret_cast<const char*>(a.ws_ml) - si));
+  }
   return kvq::launch_decode(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -21,7 +21,8 @@ EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
            "kvq_paged_decode_workspace_size", "kvq_paged_decode_attention", "kvq_dequant_page",
            "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step",
            "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention", "kvq_pc_write_pages",
-           "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention", "kvq_paged_decode_bf16_workspace_size")
+           "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention", "kvq_paged_decode_bf16_workspace_size",
+           "kvq_paged_decode_attention_noalloc")
 
 
 class KVQError(RuntimeError):
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
     L.kvq_paged_decode_attention.argtypes = [
         _p, _i32, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
         _p, _p, _sz, _i32, _p]
+    L.kvq_paged_decode_attention_noalloc.restype = _i32
+    L.kvq_paged_decode_attention_noalloc.argtypes = [
+        _p, _i32, _p, _p, _p, _p, _i32, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+        _p, _i32, _p]
     L.kvq_dequant_page.restype = _i32
     L.kvq_dequant_page.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
     L.kvq_paged_prefill_workspace_size.restype = _sz
@@ -258,6 +263,38 @@ def paged_decode_attention(q: torch.Tensor, cache: PagedKVCache, block_table: to
         hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32), ws_ptr, ws_bytes,
         pages_per_split, _stream(stream))
     _check(st, "kvq_paged_decode_attention")
+    return out
+
+
+# Bytes of the fixed scratch behind kvq_paged_decode_attention_noalloc (KVQ_DECODE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def paged_decode_attention_noalloc(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
+                                   context_lens: torch.Tensor, max_context_len: int, hadamard_block: int,
+                                   out: torch.Tensor, softmax_scale: float = 0.0, q_prerotated: int = 0,
+                                   pages_per_split: int = 0, stream=None) -> torch.Tensor:
+    """kvq_paged_decode_attention_noalloc: the decode with its split partials in the library's fixed
+    scratch; nothing is allocated (``out`` is the caller's). Calls that overlap on one GPU race."""
+    cache._check_layout()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    bsz, hq, _ = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous [B, max_pages] int32 tensor")
+    if context_lens.shape != (bsz,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be a contiguous [B] int32 tensor")
+    if tuple(out.shape) != (bsz, hq, HEAD_DIM) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, Hq, 128] float32 tensor")
+    st = lib().kvq_paged_decode_attention_noalloc(
+        _dev(q, "q", torch.bfloat16), q_prerotated,
+        _dev(cache.k_codes, "k_codes", torch.uint8), _dev(cache.v_codes, "v_codes", torch.uint8),
+        _dev(cache.k_sz, "k_sz", torch.float32), _dev(cache.v_sz, "v_sz", torch.float32),
+        cache.num_pages, cache.page_size, _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), max_context_len, bsz, hq, cache.num_kv_heads, HEAD_DIM,
+        hadamard_block, cache.bits, float(softmax_scale), _dev(out, "out", torch.float32), pages_per_split,
+        _stream(stream))
+    _check(st, "kvq_paged_decode_attention_noalloc")
     return out
 
 
