@@ -17,43 +17,10 @@
 
 #include "kvq_device.h"
 #include "kvq_launch.h"
+#include "kvq_mfma.h"
 
 namespace kvq {
 namespace {
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLazy = 8.0f;  // rescale the accumulators only when the maximum grows by more (log2 units)
-
-__device__ __forceinline__ v8bf as_bf(v4u x) { return __builtin_bit_cast(v8bf, x); }
-
-typedef __attribute__((address_space(4))) const int32_t const_i32;
-__device__ __forceinline__ int32_t ro_load(const int32_t* p, int64_t i) { return ((const_i32*)(p))[i]; }
-
-__device__ __forceinline__ float max_over_rows(float v) {
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-}
-
-// bf16 hi (truncated) + lo (rounded remainder) of four floats, packed in pairs.
-__device__ __forceinline__ void split_bf16(const float (&w)[4], uint32_t (&hi)[2], uint32_t (&lo)[2]) {
-  uint32_t hb[4];
-  uint32_t lb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    hb[i] = __float_as_uint(w[i]) & 0xFFFF0000u;
-    lb[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(w[i] - __uint_as_float(hb[i])));
-  }
-  hi[0] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
-  hi[1] = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-  lo[0] = lb[0] | (lb[1] << 16);
-  lo[1] = lb[2] | (lb[3] << 16);
-}
 
 // Loads of one 16-token tile for one lane: K rows (A operand of the four QK k-steps) and the V
 // words of the lane's channel in each of the eight 16-channel blocks.
@@ -171,8 +138,8 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_kernel(const DecodeBf16Args
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sr[i]);
     mt = max_over_rows(mt);
-    if (__any(mt > m_run + kLazy)) {
-      const float m_new = (mt > m_run + kLazy) ? mt : m_run;
+    if (__any(mt > m_run + kLazyRescale)) {
+      const float m_new = (mt > m_run + kLazyRescale) ? mt : m_run;
       const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_part *= alpha;
@@ -191,8 +158,8 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_kernel(const DecodeBf16Args
       l_part += p[i];
     }
     uint32_t h0[2], l0[2], h1[2], l1[2];
-    split_bf16({p[0], p[1], p[2], p[3]}, h0, l0);
-    split_bf16({p[4], p[5], p[6], p[7]}, h1, l1);
+    split_bf16({p[0], p[1], p[2], p[3]}, h0[0], h0[1], l0[0], l0[1]);
+    split_bf16({p[4], p[5], p[6], p[7]}, h1[0], h1[1], l1[0], l1[1]);
     const v8bf p_hi = as_bf(v4u{h0[0], h0[1], h1[0], h1[1]});
     const v8bf p_lo = as_bf(v4u{l0[0], l0[1], l1[0], l1[1]});
     // masked tokens may hold anything in the cache (even NaN): zero their V entries

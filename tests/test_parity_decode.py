@@ -133,6 +133,33 @@ def test_decode_split_invariance():
         assert np.all(H.rel_l2(o, outs[0]) < 1e-3)
 
 
+def test_decode_side_stream_own_workspace():
+    """Calls on a side stream that pass no workspace: the wrapper allocates each call's split
+    workspace with that stream current, so the memory it frees at return cannot be handed to work
+    on another stream while the call may still run. The current stream allocates and fills fresh
+    memory right after every call; every result equals the same call made on the current stream."""
+    shape = W.config("llama3_8b", batch=2)
+    lens = (900, 400)
+    _say("decode on a side stream with the wrapper's own workspace")
+    s, plan, cache = _oracle_cache(shape, lens)
+    dev = H.upload_cache(cache)
+    q = H.to_dev_bf16(W.draw_q(s))
+    bt, ln = H.to_dev(plan.block_table), H.to_dev(np.asarray(lens, dtype=np.int32))
+    assert kvq.decode_workspace_size(2, s.num_q_heads, s.num_kv_heads, 900, 16, 4) > 0
+    ref = kvq.paged_decode_attention(q, dev, bt, ln, 900, s.hadamard_block, pages_per_split=4)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    outs = [torch.empty_like(ref) for _ in range(6)]
+    junk = []
+    for o in outs:
+        kvq.paged_decode_attention(q, dev, bt, ln, 900, s.hadamard_block, out=o, pages_per_split=4, stream=side)
+        junk.append(torch.full((1 << 20,), 0xFF, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref), f"side-stream call {i} differs from the current-stream call"
+
+
 @pytest.mark.parametrize("tensor", ["k", "v"])
 @pytest.mark.parametrize("bits,ts,hb", [(4, 0, 32), (2, 1, 128), (4, 0, 1)])
 def test_dequant_page(tensor, bits, ts, hb):
@@ -159,23 +186,27 @@ def test_dequant_page(tensor, bits, ts, hb):
 # ----------------------------------------------------------------------------- full sizes
 
 def _full_size_sampled(name, n_samples, layer=0, longest=False):
+    """The whole workload in one launch (the library's split plan, as the benchmark runs it); every
+    query head of n_samples sampled (sequence, KV head) items compared with the oracle (the oracle
+    gathers an item's sequence once, so the whole group costs no more than one head)."""
     shape = W.config(name)
     lens = shape.context_lens
-    _say(f"decode full {name} lens={lens[0]}..{max(lens)}x{len(lens)} (sampled)")
+    _say(f"decode full {name} lens={lens[0]}..{max(lens)}x{len(lens)} (sampled items)")
     s, plan, cache = _oracle_cache(shape, lens, layer=layer, fast=True)
     q = W.draw_q(s, layer=layer)
     got = _gpu_decode(s, plan, H.upload_cache(cache), q, lens)
     assert np.all(np.isfinite(got))
+    g = s.num_q_heads // s.num_kv_heads
     rng = np.random.default_rng(99)
-    heads = {(int(b), int(h)) for b, h in zip(rng.integers(0, s.batch, n_samples),
-                                              rng.integers(0, s.num_q_heads, n_samples))}
-    if longest:  # the sequence with the most splits, one head of each KV head's group
+    items = {(int(b), int(kvh)) for b, kvh in zip(rng.integers(0, s.batch, n_samples),
+                                                  rng.integers(0, s.num_kv_heads, n_samples))}
+    if longest:  # the sequence with the most splits, every KV head
         b_max = int(np.argmax(lens))
-        heads |= {(b_max, kvh * (s.num_q_heads // s.num_kv_heads)) for kvh in range(s.num_kv_heads)}
-    heads = sorted(heads)
+        items |= {(b_max, kvh) for kvh in range(s.num_kv_heads)}
+    heads = sorted((b, kvh * g + j) for b, kvh in items for j in range(g))
     ref = O.decode(cache, q, plan.block_table, np.array(lens), s.num_kv_heads, s.hadamard_block, heads=heads)
     worst = H.check_attention(got, ref, f"full {name}", heads=heads)
-    _say(f"  {len(heads)} sampled heads, worst rel-L2 {worst:.2e}")
+    _say(f"  {len(items)} sampled items, {len(heads)} heads, worst rel-L2 {worst:.2e}")
 
 
 def test_decode_full_llama3_8b():
