@@ -56,6 +56,7 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   float s[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (TOKEN_SCALE) {
     // RMS in double precision across the 128 channels (16 lanes x 8), rounded once to float.
+    bool plain = true;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       double ss = 0.0;
@@ -65,9 +66,23 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
       float si = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
       if (si == 0.0f) si = 1.0f;
       s[i] = si;
-      const float rs = 1.0f / si;
+      plain = plain && si >= kFastMinScale && si < kFastMaxScale;
+    }
+    if (__builtin_expect(__all(plain), 1)) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], si, rs);
+      for (int i = 0; i < 4; ++i) {
+        const float rs = rcp_rn(s[i]);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], s[i], rs);
+      }
+    } else {
+      // a subnormal, tiny or huge RMS somewhere in the wave: IEEE division for the whole wave (the
+      // reciprocal would overflow, or the correction step's residual underflow; inside the range
+      // both give the correctly rounded quotient)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) y[n][i] = y[n][i] / s[i];
     }
   }
   float mn[4], mx[4];

@@ -96,9 +96,16 @@ __device__ __forceinline__ uint32_t rotate_quantize_row(float (&x)[8], const Row
     ss = row16_sum_f64(ss);
     s = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
     if (s == 0.0f) s = 1.0f;
-    const float rs = 1.0f / s;
+    if (s >= 0x1p-100f && s < 0x1p101f) {
+      const float rs = rcp_rn(s);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = div_rn(x[k], s, rs);
+      for (int k = 0; k < 8; ++k) x[k] = div_rn(x[k], s, rs);
+    } else {
+      // a subnormal, tiny or huge RMS: IEEE division (its reciprocal would overflow, or the
+      // correction step's residual underflow)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = x[k] / s;
+    }
   }
   float mn = fminf(fminf(fminf(x[0], x[1]), fminf(x[2], x[3])), fminf(fminf(x[4], x[5]), fminf(x[6], x[7])));
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -108,12 +115,18 @@ __device__ __forceinline__ uint32_t rotate_quantize_row(float (&x)[8], const Row
   const float delta = (mx - mn) / kQmax;  // IEEE division
   uint32_t packed = 0;
   if (delta != 0.0f) {
-    const float r = 1.0f / delta;
     // clamped to [0, qmax] before the packing rounds to an integer: the same codes as rounding first,
     // since both bounds are integers
     float c[8];
+    if (delta >= 0x1p-100f && delta < 0x1p101f) {
+      const float r = rcp_rn(delta);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(div_rn(x[k] - mn, delta, r), 0.0f), kQmax);
+      for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf(div_rn(x[k] - mn, delta, r), 0.0f), kQmax);
+    } else {
+      // a tiny or huge scale: IEEE division (see above)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) c[k] = fminf(fmaxf((x[k] - mn) / delta, 0.0f), kQmax);
+    }
     packed = pack_codes<BITS>(c);
   }
   scale = delta * s;

@@ -135,6 +135,11 @@ def test_append_skips_strides_and_degenerate_tokens():
     k[10] = 0                                              # all-zero vectors (scale 0, and RMS 0)
     v[11] = W.f32_to_bf16_bits(np.full((8, 128), 3.5, dtype=np.float32))   # constant vectors
     k[12, :, 0] = W.f32_to_bf16_bits(np.full(8, 3.0e4, dtype=np.float32))  # one huge outlier
+    # tokens whose RMS and scale lie far outside [2^-100, 2^101): tiny (about 1e-33) and huge (about
+    # 1e31) normal values, which take the division's guarded path
+    r = np.random.default_rng(13)
+    k[13] = W.f32_to_bf16_bits((r.standard_normal((8, 128)) * 1e-33).astype(np.float32))
+    v[14] = W.f32_to_bf16_bits((r.standard_normal((8, 128)) * 1e31).astype(np.float32))
     for bits, ts in ((4, 0), (2, 1)):
         got = H.download_cache(_gpu_append(k, v, slots, plan.num_pages, 8, bits, 32, ts, stride_pad=3))
         ref = O.PagedCache(plan.num_pages, 8, 16, 128, bits)

@@ -65,6 +65,40 @@ def test_decode_step_parity(name, overrides, lens, pps):
     _say(f"  worst rel-L2 {worst:.2e}")
 
 
+@pytest.mark.parametrize("bits,ts", [(4, 0), (2, 1)])
+def test_decode_step_extreme_new_tokens(bits, ts):
+    """New tokens whose RMS and scale lie far outside [2^-100, 2^101) (tiny, about 1e-33, and huge,
+    about 1e31, normal values) take the fused quantizer's guarded division; the cache rows and the
+    attention still match the oracle's append followed by its decode."""
+    shape = W.config("llama3_8b", batch=4, bits=bits, token_scale=ts)
+    lens = (40, 17, 100, 64)
+    _say(f"decode step extreme new tokens INT{bits} token scale {ts}")
+    prev = tuple(n - 1 for n in lens)
+    s = shape.with_(context_lens=prev)
+    plan = W.plan_pages(s, extra_tokens=1)
+    seq, pos = W.prefill_order(s)
+    k, v = W.draw_kv(s, len(seq))
+    cache = O.PagedCache(plan.num_pages, s.num_kv_heads, s.page_size, s.head_dim, s.bits)
+    d1 = O.append(cache, k, v, W.slots_for_positions(plan, s.page_size, seq, pos), s.hadamard_block, s.token_scale)
+    dev = H.upload_cache(cache)
+    r = np.random.default_rng(31)
+    mags = np.array([1e-33, 1e31, 1e-33, 1.0])[:, None, None]
+    kn = W.f32_to_bf16_bits((r.standard_normal((4, s.num_kv_heads, 128)) * mags).astype(np.float32))
+    vn = W.f32_to_bf16_bits((r.standard_normal((4, s.num_kv_heads, 128)) * mags[::-1]).astype(np.float32))
+    new_slots = W.slots_for_positions(plan, s.page_size, np.arange(4), np.array(lens) - 1).astype(np.int64)
+    d2 = O.append(cache, kn, vn, new_slots, s.hadamard_block, s.token_scale)
+    q = W.draw_q(s)
+    ref = O.decode(cache, q, plan.block_table, np.array(lens), s.num_kv_heads, s.hadamard_block)
+    max_len = max(lens)
+    out = kvq.decode_step(H.to_dev_bf16(q), H.to_dev_bf16(kn), H.to_dev_bf16(vn), dev, H.to_dev(plan.block_table),
+                          H.to_dev(np.asarray(lens, dtype=np.int32)), max_len, s.hadamard_block,
+                          token_scale=s.token_scale)
+    torch.cuda.synchronize()
+    H.check_attention(out.cpu().numpy(), ref, f"extreme INT{bits}")
+    compare_caches(H.download_cache(dev), cache, [(W.slots_for_positions(plan, s.page_size, seq, pos), d1),
+                                                  (new_slots, d2)], f"extreme INT{bits}")
+
+
 def test_decode_step_matches_separate_calls():
     """One fused launch and the two separate calls (append, then attention) leave the same cache
     and the same attention within the attention tolerance."""
