@@ -58,13 +58,16 @@ struct LaneOffsets {
 constexpr int kCodeAux = 2;
 
 // Loads one tile whose first token row (in the [page][head][token] row numbering shared by the
-// code and scale/zero arrays) is row0.
+// code and scale/zero arrays) is row0. A tile that is not live (past the split's end, or on a page
+// id outside the pool) loads its codes through a zero-size buffer resource: the same instructions
+// issue (fixed wait counts) and return zeros without touching memory.
 template <int BITS>
-__device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t row0, const LaneOffsets& lo) {
+__device__ __forceinline__ TileCodes load_tile(const DecodeArgs& a, int64_t row0, const LaneOffsets& lo, bool live) {
   constexpr int kRowShift = (BITS == 4) ? 6 : 5;  // log2(bytes per token row)
   const int64_t off = row0 << kRowShift;
-  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + off, 16 << kRowShift);
-  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + off, 16 << kRowShift);
+  const uint32_t bytes = live ? (16u << kRowShift) : 0u;
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(a.k_codes + off, bytes);
+  const __amdgpu_buffer_rsrc_t vr = tile_rsrc(a.v_codes + off, bytes);
   TileCodes t;
   if constexpr (BITS == 4) {
     t.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, lo.k, 0, kCodeAux));
@@ -182,6 +185,18 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + R, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], int xor_mask) {
+  const float m2 = __shfl_xor(m, xor_mask);
+  const float l2 = __shfl_xor(l, xor_mask);
+  const float mn = fmaxf(m, m2);
+  const float fa = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+  const float fb = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+  l = l * fa + l2 * fb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = o[i] * fa + __shfl_xor(o[i], xor_mask) * fb;
+  m = mn;
+}
+
 // MQ = false: decode, one query per sequence. The 16 columns of the QK output are F = 2 tile slots
 // of W = 8 columns: column n holds query head n % W (used while below g <= 8) against the tokens
 // of tile n / W of the step, so one output carries the scores of both of the step's tiles and
@@ -192,20 +207,33 @@ __device__ __forceinline__ float row_ror(float v) {
 // (query token, head) pairs of one KV head, column c meaning query c / g, head c % g, each with
 // its own causal length.
 // NT = 2 tiles per step, three step buffers.
-template <int BITS, bool PS16, int NT, bool MQ, int F>
-__global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
+// WG = 4 (one query per sequence, a sequence in several splits): a workgroup holds the WG splits
+// 4 j .. 4 j + 3 of one (sequence, KV head) item, one per wave. Each wave walks its own pages as
+// above; at the end the waves combine their (maximum, sum, accumulator) rows in LDS (log-sum-exp),
+// so one partial per group reaches memory - and with at most WG splits the group finishes the
+// rows itself, with no merge launch. WG = 1: one wave per workgroup, one partial per split.
+template <int BITS, bool PS16, int NT, bool MQ, int F, int WG>
+__global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(F == 1 || F == 2, "pack factor");
   static_assert(NT == 2, "a step is one PV chunk of two tiles");
   static_assert(!MQ || F == 1, "several queries fill the 16 columns themselves");
+  static_assert(WG == 1 || (!MQ && F == 2 && WG == 4), "split groups: one query per sequence");
   constexpr int W = 16 / F;   // columns per tile slot
   constexpr int KG = NT / F;  // packed score groups per step
   constexpr int P = 4 * KG;   // scores per lane per step
   constexpr int kQRows = MQ ? 16 : 8;  // query vectors staged per wave
-  __shared__ float qs[kQRows][kHeadDim];
-  __shared__ float4 szs[2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
-  __shared__ float4 red[F > 1 ? 16 : 1][kHeadDim / 4];  // accumulator rows, for the sum over tile slots
+  // per wave of the workgroup
+  __shared__ float qs_all[WG][kQRows][kHeadDim];
+  __shared__ float4 szs_all[WG][2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
+  __shared__ float4 red_all[WG][F > 1 ? 16 : 1][kHeadDim / 4];  // accumulator rows, for the sum over tile slots
+  __shared__ float2 cml[WG][8];  // split groups: each wave's (maximum, sum) per head
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform across the wave: kept in a scalar register
+  const int wv = (WG == 1) ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  float (&qs)[kQRows][kHeadDim] = qs_all[wv];
+  float4 (&szs)[2][NT][16] = szs_all[wv];
+  float4 (&red)[F > 1 ? 16 : 1][kHeadDim / 4] = red_all[wv];
   const int G = lane >> 4;
   const int n = lane & 15;
   const int u_l = n / W;  // tile slot of this lane's column
@@ -216,7 +244,8 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   // XCD's L2.
   const uint32_t items = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads);
   const uint32_t item = MQ ? 0u : blockIdx.x % items;
-  const int split = MQ ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x / items);
+  const int group = MQ ? 0 : static_cast<int>(blockIdx.x / items);  // split group (WG = 4) or split
+  const int split = MQ ? static_cast<int>(blockIdx.x) : group * WG + wv;
   const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads)
                      : static_cast<int>(item % static_cast<uint32_t>(a.num_kv_heads));
   const int c0 = MQ ? 16 * static_cast<int>(blockIdx.y / a.num_kv_heads) : 0;  // first column of the tile
@@ -232,8 +261,9 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   const int extra = max(0, n_pages - a.num_splits * a.pages_per_split);
   const bool extra_first = a.fused && extra > 0 && a.num_splits > 1;
   const int p_begin = split * a.pages_per_split + ((extra_first && split > 0) ? extra : 0);
-  const int p_end = extra_first ? min(n_pages, (split + 1) * a.pages_per_split + extra)
-                                : ((split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split));
+  const int p_end = (split >= a.num_splits) ? p_begin  // a group's waves past the last split: no pages
+                    : extra_first ? min(n_pages, (split + 1) * a.pages_per_split + extra)
+                                  : ((split == a.num_splits - 1) ? n_pages : min(n_pages, p_begin + a.pages_per_split));
   // queries of this sequence (MQ; never more than its tokens) and the tile's valid columns
   const int qlen = MQ ? min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len) : 1;
   const int ncols = MQ ? min(16, qlen * g - c0) : g;
@@ -260,7 +290,70 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     }
   }
 
+  const LaneFwht lf = lane_fwht(a.rot, n);
+  // ---- split groups: the waves' rows combined in LDS - each wave's (max, sum) per head and its
+  // accumulator rows (zero term included) in its own accumulator block - then a log-sum-exp over
+  // the group's splits: wave wv takes heads wv, wv + 4, row group G the row of wave G, combined
+  // across the four row groups. With one group the rows are finished here (normalised, rotated
+  // back, stored); otherwise the group's partial goes to the workspace for the merge.
+  constexpr int S = (F == 1) ? 4 : W / 4;  // output heads per lane at the end of the walk
+  const int num_groups = (a.num_splits + WG - 1) / WG;
+  auto group_finish = [&](const float (&ov)[S][8], const float (&lrow)[S], const float (&zrow)[S],
+                          const float (&mrow)[S]) {
+    float* const mine = reinterpret_cast<float*>(&red[0][0]);  // rows [head][128] (after the slot sums)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = G + 4 * s;
+      float4* dst = reinterpret_cast<float4*>(mine + c * kHeadDim + 8 * n);
+      const float zr = zrow[s];
+      dst[0] = make_float4(ov[s][0] + zr, ov[s][1] + zr, ov[s][2] + zr, ov[s][3] + zr);
+      dst[1] = make_float4(ov[s][4] + zr, ov[s][5] + zr, ov[s][6] + zr, ov[s][7] + zr);
+      if (n == 0) cml[wv][c] = make_float2(mrow[s], lrow[s]);
+    }
+    __syncthreads();
+    const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
+    for (int c = wv; c < g; c += WG) {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&red_all[G][0][0]) +
+                                                          c * kHeadDim + 8 * n);
+      const float4 ra = src[0], rb = src[1];
+      float o[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+      float mm = cml[G][c].x, ll = cml[G][c].y;
+      lse_combine(mm, ll, o, 16);
+      lse_combine(mm, ll, o, 32);
+      if (num_groups == 1) {
+        const float inv_l = (ll > 0.f) ? 1.0f / ll : 0.f;  // an empty sequence yields zeros
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] *= inv_l;
+        fwht_row16_planned(o, a.rot, lf);  // R^T = R: back to the original basis
+        if (G == 0) {
+          float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf.pos);
+          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      } else if (G == 0) {
+        const int64_t row = group * pairs + col_row(c);
+        float4* dst = reinterpret_cast<float4*>(a.ws_acc + row * kHeadDim + 8 * n);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        if (n == 0) reinterpret_cast<float2*>(a.ws_ml)[row] = make_float2(mm, ll);
+      }
+    }
+  };
+
   if (p_begin >= p_end || ncols <= 0) {
+    if constexpr (WG > 1) {  // no pages for this wave: an empty row (maximum -inf) in its group
+      float ov[S][8], lrow[S], zrow[S], mrow[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) ov[s][m] = 0.f;
+        lrow[s] = 0.f;
+        zrow[s] = 0.f;
+        mrow[s] = kNegInf;
+      }
+      group_finish(ov, lrow, zrow, mrow);
+      return;
+    }
     if (a.num_splits == 1) {  // empty sequence (or no valid query in the tile): zero output
       for (int c = G; c < ncols_rows; c += 4) {
         float4* o = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + n * 8);
@@ -286,9 +379,9 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   float z_part = 0.f;      // this lane's share of sum p (z - B delta) (head h_l)
   const float lazy = kLazyRescale;
 
-  // Page of a tile (scalar load). Tiles past the split's end read the last tile again (masked out
-  // through pg = -1), so that every fetch issues the same loads and the wait for a buffer never
-  // has to drain the loads of the next one.
+  // Page of a tile (scalar load). Tiles past the split's end issue the same loads as the others
+  // (zero-size resources: no memory traffic, masked out through pg = -1), so that the wait for a
+  // buffer never has to drain the loads of the next one.
   LaneOffsets lo;
   lo.k = (BITS == 4) ? (n * (kHeadDim / 2) + 16 * G) : (n * (kHeadDim / 4) + 8 * G);
   lo.v = (BITS == 4) ? (G * 4 * (kHeadDim / 2) + 16 * n) : (G * 4 * (kHeadDim / 4) + 8 * n);
@@ -302,9 +395,10 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
       const int tt = min(t + u, last_tile);
       const int32_t p = ro_load(bt, PS16 ? tt : tt / tiles_per_page);
       const bool ok = (p >= 0 && p < a.num_pages);
-      pg[u] = (ok && t + u <= last_tile) ? p : -1;
+      const bool live = ok && t + u <= last_tile;
+      pg[u] = live ? p : -1;
       const int64_t row0 = (ok ? p : 0) * page_rows + head_rows + (PS16 ? 0 : 16 * (tt % tiles_per_page));
-      x[u] = load_tile<BITS>(a, row0, lo);
+      x[u] = load_tile<BITS>(a, row0, lo, live);
     }
   };
 
@@ -324,7 +418,6 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   fetch(tile_begin + NT, x1, pg1);
 
   // ---- query: rotate (R q), scale by softmax_scale * log2(e), stage in LDS in natural order
-  const LaneFwht lf = lane_fwht(a.rot, n);
 #pragma unroll
   for (int r = 0; r < kQPerGroup; ++r) {
     const int c = 4 * r + G;
@@ -590,7 +683,6 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
   }
   // S output heads per lane: F = 1: heads 4G + s, straight from the accumulator rows; F > 1:
   // heads G + 4s, the sum of their F slot rows, exchanged through LDS.
-  constexpr int S = (F == 1) ? 4 : W / 4;
   float ov[S][8];
   int hh[S];
   if constexpr (F == 1) {
@@ -646,6 +738,11 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
     return;
   }
 
+  if constexpr (WG > 1) {
+    group_finish(ov, lrow, zrow, mrow);
+    return;
+  }
+
   // Split: publish this split's partial (un-normalised accumulator with its zero term, running
   // maximum and sum) for the merge kernel.
   const int64_t pairs = static_cast<int64_t>(a.batch) * (MQ ? a.q_len_max : 1) * a.num_q_heads;
@@ -668,18 +765,6 @@ __global__ __launch_bounds__(64, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(c
 // loaded with independent loads before any is combined, so 32 splits cost one memory round trip.
 // The four groups' running (max, sum, vector) are then combined across rows, rotated back and
 // stored by row group 0.
-__device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], int xor_mask) {
-  const float m2 = __shfl_xor(m, xor_mask);
-  const float l2 = __shfl_xor(l, xor_mask);
-  const float mn = fmaxf(m, m2);
-  const float fa = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-  const float fb = (m2 == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-  l = l * fa + l2 * fb;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = o[i] * fa + __shfl_xor(o[i], xor_mask) * fb;
-  m = mn;
-}
-
 __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const int G = lane >> 4;
@@ -771,15 +856,16 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   }
 }
 
-template <bool MQ, int F, int NT>
+template <bool MQ, int F, int NT, int WG>
 hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const bool ps16 = a.page_size == 16;
+  const dim3 block(64 * WG);
   if (a.bits == 4) {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, NT, MQ, F>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, NT, MQ, F>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, NT, MQ, F, WG>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<4, false, NT, MQ, F, WG>), grid, block, 0, stream, a);
   } else {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, NT, MQ, F>), grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, NT, MQ, F>), grid, dim3(64), 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, NT, MQ, F, WG>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, NT, MQ, F, WG>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -795,9 +881,26 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
                                     static_cast<unsigned>(a.batch))
                              : dim3(static_cast<unsigned>(a.num_splits) * static_cast<unsigned>(a.batch) *
                                     static_cast<unsigned>(a.num_kv_heads));
-  // g <= 8 with one query per sequence (checked by the caller): two tile slots
-  const hipError_t e =
-      a.q_lens ? launch_kernel<true, 1, 2>(a, grid, stream) : launch_kernel<false, 2, 2>(a, grid, stream);
+  if (a.q_lens) {
+    const hipError_t e = launch_kernel<true, 1, 2, 1>(a, grid, stream);
+    if (e != hipSuccess || a.num_splits == 1) return e;
+    return launch_decode_merge(a, stream);
+  }
+  // One query per sequence (g <= 8, checked by the caller: two tile slots). A split sequence runs in
+  // groups of four splits per workgroup, which combine their partials in LDS (while the grid of
+  // 256-thread workgroups stays below 2^32 work-items; otherwise one split per workgroup).
+  const uint64_t items = static_cast<uint64_t>(a.batch) * static_cast<uint64_t>(a.num_kv_heads);
+  const uint64_t groups = (static_cast<uint64_t>(a.num_splits) + 3) / 4;
+  if (a.num_splits > 1 && groups * items * 256 < (uint64_t{1} << 32)) {
+    const hipError_t e = launch_kernel<false, 2, 2, 4>(a, dim3(static_cast<unsigned>(groups * items)), stream);
+    if (e != hipSuccess || groups == 1) return e;
+    // the merge sees one partial per group, every group's row written (an empty one with maximum -inf)
+    DecodeArgs m = a;
+    m.num_splits = static_cast<int32_t>(groups);
+    m.all_splits = 1;
+    return launch_decode_merge(m, stream);
+  }
+  const hipError_t e = launch_kernel<false, 2, 2, 1>(a, grid, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   return launch_decode_merge(a, stream);
 }
