@@ -207,11 +207,11 @@ __device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], i
 // (query token, head) pairs of one KV head, column c meaning query c / g, head c % g, each with
 // its own causal length.
 // NT = 2 tiles per step, three step buffers.
-// WG = 4 (one query per sequence, a sequence in several splits): a workgroup holds the WG splits
+// WG = 4 (one query per sequence, a sequence in many splits): a workgroup holds the WG splits
 // 4 j .. 4 j + 3 of one (sequence, KV head) item, one per wave. Each wave walks its own pages as
 // above; at the end the waves combine their (maximum, sum, accumulator) rows in LDS (log-sum-exp),
-// so one partial per group reaches memory - and with at most WG splits the group finishes the
-// rows itself, with no merge launch. WG = 1: one wave per workgroup, one partial per split.
+// so one partial per group reaches memory for the merge. WG = 1: one wave per workgroup, one
+// partial per split.
 template <int BITS, bool PS16, int NT, bool MQ, int F, int WG>
 __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(F == 1 || F == 2, "pack factor");
@@ -222,18 +222,21 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
   constexpr int KG = NT / F;  // packed score groups per step
   constexpr int P = 4 * KG;   // scores per lane per step
   constexpr int kQRows = MQ ? 16 : 8;  // query vectors staged per wave
-  // per wave of the workgroup
-  __shared__ float qs_all[WG][kQRows][kHeadDim];
+  // Per wave of the workgroup: the query rows (prologue only) and the accumulator rows (epilogue
+  // only) share one block; the scale/zero staging of the walk has its own.
+  constexpr int kRedRows = F > 1 ? 16 : 1;
+  constexpr int kQsRedBytes = std::max(kQRows * kHeadDim * 4, kRedRows * kHeadDim * 4);
+  __shared__ __attribute__((aligned(16))) uint8_t qsred_all[WG][kQsRedBytes];
   __shared__ float4 szs_all[WG][2][NT][16];  // scale/zero of a step's tiles, two steps: [buf][tile][K 0..31 | V 32..63]
-  __shared__ float4 red_all[WG][F > 1 ? 16 : 1][kHeadDim / 4];  // accumulator rows, for the sum over tile slots
   __shared__ float2 cml[WG][8];  // split groups: each wave's (maximum, sum) per head
 
   const int lane = threadIdx.x & 63;
   // the wave index is uniform across the wave: kept in a scalar register
   const int wv = (WG == 1) ? 0 : __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  float (&qs)[kQRows][kHeadDim] = qs_all[wv];
+  float (&qs)[kQRows][kHeadDim] = *reinterpret_cast<float (*)[kQRows][kHeadDim]>(&qsred_all[wv][0]);
   float4 (&szs)[2][NT][16] = szs_all[wv];
-  float4 (&red)[F > 1 ? 16 : 1][kHeadDim / 4] = red_all[wv];
+  // accumulator rows, for the sum over tile slots (and, in split groups, the rows to combine)
+  float4 (&red)[kRedRows][kHeadDim / 4] = *reinterpret_cast<float4 (*)[kRedRows][kHeadDim / 4]>(&qsred_all[wv][0]);
   const int G = lane >> 4;
   const int n = lane & 15;
   const int u_l = n / W;  // tile slot of this lane's column
@@ -294,10 +297,8 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
   // ---- split groups: the waves' rows combined in LDS - each wave's (max, sum) per head and its
   // accumulator rows (zero term included) in its own accumulator block - then a log-sum-exp over
   // the group's splits: wave wv takes heads wv, wv + 4, row group G the row of wave G, combined
-  // across the four row groups. With one group the rows are finished here (normalised, rotated
-  // back, stored); otherwise the group's partial goes to the workspace for the merge.
+  // across the four row groups; the group's partial goes to the workspace for the merge.
   constexpr int S = (F == 1) ? 4 : W / 4;  // output heads per lane at the end of the walk
-  const int num_groups = (a.num_splits + WG - 1) / WG;
   auto group_finish = [&](const float (&ov)[S][8], const float (&lrow)[S], const float (&zrow)[S],
                           const float (&mrow)[S]) {
     float* const mine = reinterpret_cast<float*>(&red[0][0]);  // rows [head][128] (after the slot sums)
@@ -313,24 +314,14 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
     __syncthreads();
     const int64_t pairs = static_cast<int64_t>(a.batch) * a.num_q_heads;
     for (int c = wv; c < g; c += WG) {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&red_all[G][0][0]) +
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(&qsred_all[G][0]) +
                                                           c * kHeadDim + 8 * n);
       const float4 ra = src[0], rb = src[1];
       float o[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
       float mm = cml[G][c].x, ll = cml[G][c].y;
       lse_combine(mm, ll, o, 16);
       lse_combine(mm, ll, o, 32);
-      if (num_groups == 1) {
-        const float inv_l = (ll > 0.f) ? 1.0f / ll : 0.f;  // an empty sequence yields zeros
-#pragma unroll
-        for (int m = 0; m < 8; ++m) o[m] *= inv_l;
-        fwht_row16_planned(o, a.rot, lf);  // R^T = R: back to the original basis
-        if (G == 0) {
-          float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf.pos);
-          dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-          dst[1] = make_float4(o[4], o[5], o[6], o[7]);
-        }
-      } else if (G == 0) {
+      if (G == 0) {
         const int64_t row = group * pairs + col_row(c);
         float4* dst = reinterpret_cast<float4*>(a.ws_acc + row * kHeadDim + 8 * n);
         dst[0] = make_float4(o[0], o[1], o[2], o[3]);
@@ -856,6 +847,8 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   }
 }
 
+constexpr int kMinSplitsGrouped = 16;
+
 template <bool MQ, int F, int NT, int WG>
 hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const bool ps16 = a.page_size == 16;
@@ -889,11 +882,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   // One query per sequence (g <= 8, checked by the caller: two tile slots). A split sequence runs in
   // groups of four splits per workgroup, which combine their partials in LDS (while the grid of
   // 256-thread workgroups stays below 2^32 work-items; otherwise one split per workgroup).
+  // Only items with many splits are grouped: a group's workgroup keeps its LDS until its slowest wave
+  // ends, so with few splits per item (a large or ragged batch, where many of a group's waves would
+  // have no pages) one split per workgroup keeps more waves busy.
   const uint64_t items = static_cast<uint64_t>(a.batch) * static_cast<uint64_t>(a.num_kv_heads);
   const uint64_t groups = (static_cast<uint64_t>(a.num_splits) + 3) / 4;
-  if (a.num_splits > 1 && groups * items * 256 < (uint64_t{1} << 32)) {
+  if (a.num_splits >= kMinSplitsGrouped && groups * items * 256 < (uint64_t{1} << 32)) {
     const hipError_t e = launch_kernel<false, 2, 2, 4>(a, dim3(static_cast<unsigned>(groups * items)), stream);
-    if (e != hipSuccess || groups == 1) return e;
+    if (e != hipSuccess) return e;
     // the merge sees one partial per group, every group's row written (an empty one with maximum -inf)
     DecodeArgs m = a;
     m.num_splits = static_cast<int32_t>(groups);

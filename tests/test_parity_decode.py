@@ -133,6 +133,25 @@ def test_decode_split_invariance():
         assert np.all(H.rel_l2(o, outs[0]) < 1e-3)
 
 
+@pytest.mark.parametrize("lens,pps", [((384, 100, 17, 250), 1), ((272, 100, 17, 250), 1), ((256, 33, 1, 200), 1),
+                                      ((640, 100, 17, 250), 2), ((1024, 64, 3, 512), 4)])
+def test_decode_split_groups(lens, pps):
+    """Sequences in 16 or more splits run four splits to a workgroup and combine them in LDS: 24, 17,
+    16, 20 and 16 splits of the longest sequence (17 leaves a group whose waves past the last split
+    have no pages), and the shorter sequences leave waves and whole groups empty (rows with maximum
+    -inf in the combine and the merge)."""
+    shape = W.config("llama3_8b", batch=4, hadamard_block=64)
+    _say(f"decode split groups lens={lens} pages_per_split={pps}")
+    s, plan, cache = _oracle_cache(shape, lens)
+    q = W.draw_q(s)
+    ref = O.decode(cache, q, plan.block_table, np.array(lens), s.num_kv_heads, s.hadamard_block)
+    got = _gpu_decode(s, plan, H.upload_cache(cache), q, lens, pps=pps)
+    H.check_attention(got, ref, f"split groups {lens} pps{pps}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0)
+
+
 def test_decode_side_stream_own_workspace():
     """Calls on a side stream that pass no workspace: the wrapper allocates each call's split
     workspace with that stream current, so the memory it frees at return cannot be handed to work
