@@ -69,8 +69,11 @@ struct DecodeArgs {
   float* out;
   int32_t num_splits;             // splits of the page range per (sequence, kv head)
   int32_t pages_per_split;
-  float* ws_acc;                  // [num_splits][batch][num_q_heads][128]
-  float* ws_ml;                   // [num_splits][batch][num_q_heads][2]  (max, sum) in log2 units
+  // Partials: [num_splits][batch][num_q_heads][128] and [..][2] (max, sum) in log2 units; with one
+  // query per sequence and 16 or more splits only the first ceil(num_splits / 4) rows are used
+  // (one per group of four splits, combined in the decode's workgroup).
+  float* ws_acc;
+  float* ws_ml;
   // Several queries per sequence (chunked prefill, speculative verification): q and out are
   // [batch][q_len_max][num_q_heads][128]; sequence b's q_lens[b] queries are its last q_lens[b]
   // tokens, causal. nullptr for the decode (one query per sequence).
