@@ -3,7 +3,8 @@
 // "Technical Deep Dive"; a paged low-bit attention kernel, OSCAR abstract on thelatestinai.com;
 // split decoding after FlashDecoding-v2, named in the OScaR abstract).
 //
-// One wave per (split, KV head, sequence); the split's pages are walked as 16-token tiles, two
+// One wave per (split, KV head, sequence) - four splits of one (sequence, KV head) to a workgroup
+// when a sequence has 16 splits or more; the split's pages are walked as 16-token tiles, two
 // tiles per step. Dequantization is folded around the contractions instead of materialised:
 //   score_j = q~ . (delta_j c_j + z_j 1) = delta_j (q~ . c_j) + z_j sum(q~)
 //   sum_j p_j v_j = sum_j (p_j delta_j) c_j + sum_j p_j z_j 1
