@@ -338,13 +338,20 @@ class Ceiling:
         """A decode launch: one 64-lane workgroup per split wave, reading ``nbytes``."""
         return self.measure("read-only, non-temporal", nbytes, 0, 32, 0, waves, 64, stream)
 
-    def for_append(self, token_heads, bits, stream, patterns=("mix",)):
-        """An append launch (one wave per 16-token item, four per 256-thread workgroup) moving the
-        append's bytes: 512 read and 2 (128 bits / 8) + 16 written per token-head."""
-        items = -(-token_heads // 16)  # (16-token tile, KV head) items
-        grid = -(-items // 4)
-        wr = 2 * 128 * bits // 8 + 16
-        rd = 512
+    @staticmethod
+    def append_shape(tokens, heads, bits):
+        """(workgroups, threads per workgroup, read units, write units) of an append of ``tokens``
+        tokens x ``heads`` KV heads: one wave per (16-token tile, KV head) item, four per 256-thread
+        workgroup; per token-head 512 bytes read (bf16 K and V) and 2 (128 bits / 8) + 16 written
+        (codes, scale and zero), in 16-byte units."""
+        items = -(-tokens // 16) * heads
+        return -(-items // 4), 256, 512 // 16, (2 * 128 * bits // 8 + 16) // 16
+
+    def for_append(self, tokens, heads, bits, stream, patterns=("mix",)):
+        """An append launch's shape moving the append's bytes (see append_shape)."""
+        grid, _, rd_u, wr_u = self.append_shape(tokens, heads, bits)
+        token_heads = tokens * heads
+        rd, wr = 16 * rd_u, 16 * wr_u
         out = {}
         total = token_heads * (rd + wr)
         if "mix" in patterns:
@@ -505,7 +512,7 @@ def record_oscar(dev, stream, ceiling):
     t_bf, gb_bf = _bf16_attention(shape, plan, dev, stream)
     torch_empty_cache()
     c_dec = ceiling.for_decode(b_att, waves, stream)
-    c_app = ceiling.for_append(shape.batch * shape.chunk * shape.num_kv_heads, shape.bits, stream)["mix"]
+    c_app = ceiling.for_append(shape.batch * shape.chunk, shape.num_kv_heads, shape.bits, stream)["mix"]
     t_dec = [stored_traffic(shape.name, kk) for kk in ("decode_mfma_kernel", "decode_merge_splits_kernel")]
     t_dec = None if None in t_dec else sum(t_dec)
     t_ms = float(np.mean(att))
@@ -1436,7 +1443,7 @@ def main():
         ceiling = Ceiling(dev)
         c_dec = ceiling.for_decode(b_attn, _decode_waves(shape.batch, shape.num_q_heads, shape.num_kv_heads, max_len,
                                                          shape.page_size), stream)
-        c_app = ceiling.for_append(len(seq) * shape.num_kv_heads, shape.bits, stream,
+        c_app = ceiling.for_append(len(seq), shape.num_kv_heads, shape.bits, stream,
                                    patterns=("mix", "read", "write", "copy"))
         result["ceiling"] = {"unit": "GB/s", "decode_shape": c_dec, "append_shape": c_app,
                              "note": "streaming probes (libkvq_stream.so) with the kernels' grid, workgroup size and "

@@ -90,3 +90,20 @@ def test_stored_traffic_is_tied_to_the_sources(tmp_path, monkeypatch, matching):
     monkeypatch.setattr(bench, "traffic_file", lambda workload: str(path))
     assert bench.stored_traffic("llama3_8b", "append_kernel") == (123456 if matching else None)
     assert bench.stored_traffic("llama3_8b", "decode_mfma_kernel") is None
+
+
+def test_ceiling_launch_shapes_match_the_kernels():
+    # the append: one wave per (16-token tile, KV head) item, four waves per 256-thread workgroup,
+    # 512 B read and 144 B (INT4) / 80 B (INT2) written per token-head, in 16-byte units
+    assert bench.Ceiling.append_shape(65536, 8, 4) == (8192, 256, 32, 9)   # Llama-3-8B prefill
+    assert bench.Ceiling.append_shape(32 * 512, 4, 2) == (1024, 256, 32, 5)  # one OScaR chunk
+    assert bench.Ceiling.append_shape(17, 3, 4) == (2, 256, 32, 9)          # 2 tiles x 3 heads = 6 items
+
+
+def test_decode_waves_follow_the_split_plan():
+    # one wave per (split, sequence, KV head), the splits read back from the workspace size: the
+    # three large workloads each fill 2,048 waves (16 / 64 / 16 splits per item)
+    assert bench._decode_waves(16, 32, 8, 4097, 16) == 16 * 16 * 8
+    assert bench._decode_waves(4, 64, 8, 32769, 16) == 64 * 4 * 8
+    assert bench._decode_waves(32, 28, 4, 16385, 16) == 16 * 32 * 4
+    assert bench._decode_waves(1, 8, 8, 512, 16) == 4 * 1 * 8   # 32 pages, 8 per split at least
