@@ -183,7 +183,8 @@ kvq_status kvq_paged_decode_attention(
  * before anything is launched. Every call on one GPU shares that GPU's scratch, and its contents
  * are those of the last call: calls that overlap on one GPU (other streams, other threads) race
  * and give undefined results; serialize them (e.g. one stream). The first call on a GPU looks up
- * that GPU's scratch address (a HIP runtime query, no allocation).
+ * that GPU's scratch address (a HIP runtime query, no allocation): callers that capture graphs make
+ * one call on each GPU before capturing, so that the query does not fall inside the capture.
  */
 #define KVQ_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
