@@ -87,15 +87,14 @@ def decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size
 # rocprofv3's FETCH_SIZE and WRITE_SIZE (KiB per dispatch) do not count every byte the same way
 # (FETCH_SIZE counts a 128-byte read as one 64-byte request), so each is scaled by the ratio it
 # shows on a plain 256 MiB device copy in the same run. The traffic recorded for a kernel is tied
-# to the sources it was built from: once they change, the stored figure no longer applies.
+# to what it was built from - its source files and the compiler flags of its translation unit (the
+# first file listed): once they change, the stored figure no longer applies.
 
 CSRC = os.path.join(ROOT, "paged_decode_attention_amd", "csrc")
 KERNEL_SOURCES = {
-    "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h",
-                      "../build.py"],
-    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h",
-                           "../build.py"],
-    "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "../build.py"],
+    "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
+    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
+    "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
 }
 CALIBRATION_BYTES = 256 << 20
 TRAFFIC_TAG = "traffic-json: "
@@ -103,10 +102,13 @@ TRAFFIC_TAG = "traffic-json: "
 
 def sources_sha256(kernel: str) -> str:
     import hashlib
+    from paged_decode_attention_amd import build as _build
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
             h.update(fh.read())
+    tu = KERNEL_SOURCES[kernel][0]
+    h.update(" ".join(_build.CFLAGS + _build.EXTRA_CFLAGS.get(tu, [])).encode())
     return h.hexdigest()
 
 
