@@ -28,7 +28,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 # the streaming probes that measure the HBM ceiling (measurement support, include/kvq_stream.h)
 STREAM_LIB = os.path.join(PKG, "libkvq_stream.so")
 STREAM_SOURCES = ["kvq_stream.hip"]
-SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_dequant.hip",
+SOURCES = ["kvq_api.hip", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_chunk_attn.hip", "kvq_dequant.hip",
            "kvq_baseline_bf16.hip", "kvq_pc.hip", "kvq_pc_write.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

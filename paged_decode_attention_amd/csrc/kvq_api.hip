@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "../../include/kvq.h"
+#include "kvq_chunk.h"
 #include "kvq_launch.h"
 
 namespace {
@@ -480,6 +481,7 @@ kvq_status kvq_paged_prefill_attention(
   if (!q_lens) return KVQ_ERR_NULL;
   if (!aligned(q_lens, 4)) return KVQ_ERR_SHAPE;
   a.q_lens = q_lens;
+  if (kvq::chunk_attention_applies(a)) return kvq::launch_chunk_attention(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
   return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -1,0 +1,14 @@
+// Launch interface of the large-chunk attention (kvq_chunk_attn.hip): several queries per sequence
+// with at least 128 (query, head) columns per KV head, and enough of them to fill the chip - one
+// launch, each cache tile dequantized once per 128 columns, no split partials, no workspace.
+#pragma once
+
+#include "kvq_launch.h"
+
+namespace kvq {
+
+// Whether kvq_paged_prefill_attention takes the large-chunk kernel for these (validated) arguments.
+bool chunk_attention_applies(const DecodeArgs& a);
+hipError_t launch_chunk_attention(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,133 @@
+"""GPU parity of kvq_paged_prefill_attention on large chunks - at least 128 (query, head) columns
+per KV head and 256 workgroups of them, where the library dequantizes each cache tile once per
+128 columns into LDS (fp16 operands on the matrix cores) - against the oracle's multi-query
+attention, every query row of every sequence.
+
+The shapes cover INT4 and INT2 (per-token scaling), GQA 4, 7 and 8, page sizes 16, 32 and 64,
+ragged contexts whose last tile ends mid-tile (the rows past each sequence hold the oracle
+cache's NaN poison), queries per sequence from 0 to the maximum, and a last workgroup that is
+only partly filled with columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity_helpers as H
+from oracle import kvq_oracle as O
+from paged_decode_attention_amd import kvq
+from paged_decode_attention_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _case(name, overrides, lens):
+    shape = W.config(name, **overrides).with_(context_lens=tuple(lens))
+    plan = W.plan_pages(shape, extra_tokens=0)
+    seq, pos = W.prefill_order(shape)
+    k, v = W.draw_kv(shape, len(seq))
+    cache = O.PagedCache(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.head_dim, shape.bits)
+    O.append(cache, k, v, W.slots_for_positions(plan, shape.page_size, seq, pos), shape.hadamard_block,
+             shape.token_scale)
+    return shape, plan, cache
+
+
+def _queries(shape, qmax, seed):
+    rng = np.random.default_rng(seed)
+    return W.f32_to_bf16_bits(rng.standard_normal((shape.batch, qmax, shape.num_q_heads, 128)).astype(np.float32))
+
+
+def _gpu(shape, plan, dev, q, q_lens, lens, q_prerotated=0, softmax_scale=0.0):
+    qmax = q.shape[1]
+    max_len = int(max(lens))
+    nbytes = kvq.prefill_workspace_size(shape.batch, qmax, shape.num_q_heads, shape.num_kv_heads, max_len,
+                                        shape.page_size)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((shape.batch, qmax, shape.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    kvq.paged_prefill_attention(H.to_dev_bf16(q), H.to_dev(np.asarray(q_lens, dtype=np.int32)), dev,
+                                H.to_dev(plan.block_table), H.to_dev(np.asarray(lens, dtype=np.int32)), max_len,
+                                shape.hadamard_block, softmax_scale=softmax_scale, out=out, workspace=ws,
+                                q_prerotated=q_prerotated)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _blocks(shape, qmax):
+    """Workgroups of the large-chunk launch: 128 columns each, per KV head and sequence."""
+    cols = qmax * shape.group
+    return -(-cols // 128) * shape.num_kv_heads * shape.batch
+
+
+CASES = [
+    # name, overrides, context lens, q_lens, max_q_len
+    ("oscar_int2", dict(batch=3), (700, 600, 520), (512, 300, 513), 513),                     # INT2, g 7
+    ("llama3_8b", dict(batch=4), (300, 1000, 256, 700), (256, 100, 0, 37), 256),              # INT4, g 4
+    ("llama2_70b", dict(batch=2, page_size=32), (450, 333), (256, 200), 256),                 # g 8, pages of 32
+    ("llama3_8b", dict(batch=4, page_size=64, hadamard_block=16), (129, 640, 300, 77), (129, 64, 256, 77), 256),
+]
+
+
+@pytest.mark.parametrize("name,overrides,lens,q_lens,qmax", CASES,
+                         ids=[f"{c[0]}-ps{c[1].get('page_size', 16)}" for c in CASES])
+def test_chunk_attention_parity(name, overrides, lens, q_lens, qmax):
+    shape, plan, cache = _case(name, overrides, lens)
+    assert qmax * shape.group >= 128 and _blocks(shape, qmax) >= 256, "not a large-chunk launch"
+    _say(f"chunk attention {name} {overrides} lens={lens} q_lens={q_lens}")
+    q = _queries(shape, qmax, seed=sum(lens) + qmax)
+    ref = O.multi_query_attention(cache, q, np.array(q_lens), plan.block_table, np.array(lens), shape.num_kv_heads,
+                                  shape.hadamard_block)
+    got = _gpu(shape, plan, H.upload_cache(cache), q, q_lens, lens)
+    assert np.all(np.isfinite(got))
+    for b, ql in enumerate(q_lens):
+        ql = min(ql, lens[b])
+        assert np.all(got[b, ql:] == 0), f"rows past q_lens[{b}] must be zero"
+        if ql:
+            worst = H.check_attention(got[b, :ql].reshape(-1, 128), ref[b, :ql].reshape(-1, 128), f"{name}/b{b}")
+            _say(f"  b{b}: {ql} queries, worst rel-L2 {worst:.2e}")
+
+
+def test_chunk_attention_prerotated_query():
+    """q_prerotated = 1 with R q given equals q_prerotated = 0 with q (same launch shape)."""
+    shape, plan, cache = _case("llama3_8b", dict(batch=4), (300, 280, 256, 400))
+    q_lens = (256, 256, 256, 256)
+    q = _queries(shape, 256, seed=11)
+    r = O.rotation_matrix(128, shape.hadamard_block)
+    qr = W.f32_to_bf16_bits((W.bf16_bits_to_f32(q).astype(np.float64) @ r.T).astype(np.float32))
+    _say("chunk attention, prerotated query")
+    dev = H.upload_cache(cache)
+    ref = O.multi_query_attention(cache, qr, np.array(q_lens), plan.block_table, np.array((300, 280, 256, 400)),
+                                  shape.num_kv_heads, shape.hadamard_block, q_prerotated=1)
+    got = _gpu(shape, plan, dev, qr, q_lens, (300, 280, 256, 400), q_prerotated=1)
+    worst = H.check_attention(got.reshape(-1, 128), ref.reshape(-1, 128), "prerotated")
+    _say(f"  worst rel-L2 {worst:.2e}")
+
+
+def test_chunk_attention_cache_scales():
+    """The same cache with every V (or K) scale and zero multiplied by 2^-40 or 2^40 - values far
+    outside fp16's range: the output scales by exactly that power of two for V, and does not change
+    for K when the softmax scale undoes it, so the tiles' power-of-two exponents carry the range."""
+    lens = (300, 513, 256, 77)
+    shape, plan, cache = _case("llama3_8b", dict(batch=4), lens)
+    q_lens = (256, 256, 256, 77)
+    q = _queries(shape, 256, seed=12)
+    base = _gpu(shape, plan, H.upload_cache(cache), q, q_lens, lens)
+    for tensor in ("v", "k"):
+        for e in (-40, 40):
+            scaled = O.PagedCache(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.head_dim, shape.bits)
+            for name in ("k_codes", "v_codes", "k_sz", "v_sz"):
+                setattr(scaled, name, getattr(cache, name).copy())
+            sz = getattr(cache, f"{tensor}_sz")
+            setattr(scaled, f"{tensor}_sz", (sz.astype(np.float64) * 2.0 ** e).astype(np.float32))
+            _say(f"chunk attention, {tensor.upper()} scale and zero x 2^{e}")
+            sm = 2.0 ** -e / np.sqrt(128.0) if tensor == "k" else 0.0
+            got = _gpu(shape, plan, H.upload_cache(scaled), q, q_lens, lens, softmax_scale=sm)
+            want = base.astype(np.float64) * (2.0 ** e if tensor == "v" else 1.0)
+            worst = 0.0
+            for b, ql in enumerate(q_lens):
+                assert np.all(got[b, ql:] == 0)
+                worst = max(worst, H.check_attention(got[b, :ql].reshape(-1, 128), want[b, :ql].reshape(-1, 128),
+                                                     f"{tensor} x 2^{e}"))
+            _say(f"  worst rel-L2 against the unscaled output {worst:.2e}")
