@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged INT4 decode-attn & quant-append HBM GB/s (% of MI355X peak), tokens/s"
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
 N_INPUT_COPIES = 4
 N_CACHE_COPIES = 14
 
@@ -401,6 +402,19 @@ def _say(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
+def _chunk_attention_rates(lens, qlen, num_q_heads, ms):
+    """Rates of a several-query attention call: the algorithmic QK + PV multiply-adds over every
+    query's causal window, and - for the large-chunk kernel - the fp16 matrix-core work it runs
+    (three passes per score: QK with the query's hi and lo parts, then PV, over whole 64-token
+    tiles) against the dense fp16 peak."""
+    causal = float(np.sum([qlen * (int(n) - qlen) + qlen * (qlen + 1) / 2 for n in lens]))
+    flops = 4.0 * 128 * num_q_heads * causal
+    tiles = float(np.sum([np.ceil(int(n) / 64.0) for n in lens]))
+    mfma_flops = 3 * 2.0 * 128 * 64 * tiles * qlen * num_q_heads
+    return {"attention_TFLOPs": round(flops / ms / 1e9, 2), "mfma_fp16_TFLOPs": round(mfma_flops / ms / 1e9, 1),
+            "mfma_frac_of_fp16_dense_peak": round(mfma_flops / ms / 1e9 / PEAK_FP16_TFLOPS, 3)}
+
+
 def _block_times(fn, n_blocks, per_block, stream, start=0):
     """Per-call ms of fn over n_blocks event-bracketed blocks of per_block back-to-back calls."""
     import torch
@@ -497,6 +511,22 @@ def record_oscar(dev, stream, ceiling):
     # the chunks in order, each timed on its own (one event pair per chunk): the serving loop's calls
     chunk_ms = _block_times(chunk, len(full), 1, stream)
     del k, v
+    # the attention of the last 512-token chunk over its sequence (16384 tokens): the large-chunk kernel
+    lens_c = np.asarray(shape.context_lens, dtype=np.int32)
+    gq = torch.Generator(device=dev)
+    gq.manual_seed(shape.seed + shape.chunk)
+    qc = torch.randn((shape.batch, shape.chunk, shape.num_q_heads, 128), generator=gq, device=dev).to(torch.bfloat16)
+    qlc = torch.full((shape.batch,), shape.chunk, dtype=torch.int32, device=dev)
+    btc, lens_cd = torch.from_numpy(plan.block_table).to(dev), torch.from_numpy(lens_c).to(dev)
+    outc = torch.empty((shape.batch, shape.chunk, shape.num_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def chunk_attention(i):
+        kvq.paged_prefill_attention(qc, qlc, cache, btc, lens_cd, int(lens_c.max()), shape.hadamard_block, out=outc,
+                                    stream=stream)
+    chunk_attention(0)
+    ca_ms = _block_times(chunk_attention, 3, 2, stream)
+    ca_kernel = kvq.prefill_kernel(shape.batch, shape.chunk, shape.num_q_heads, shape.num_kv_heads)
+    del qc, outc
     copies = [cache] + [kvq.PagedKVCache(cache.k_codes.clone(), cache.v_codes.clone(), cache.k_sz.clone(),
                                          cache.v_sz.clone(), cache.bits) for _ in range(7)]
     append, attend, lens = _decode_step_fns(shape, plan, copies, dev, stream)
@@ -529,6 +559,11 @@ def record_oscar(dev, stream, ceiling):
         "fused_decode_step_GBps": round((b_att + b_app) / (f_ms * 1e-3) / 1e9, 1),
         "chunk_append": dict(_pcts(chunk_ms), chunks=len(full), bytes=b_chunk,
                              tokens_per_s=round(shape.batch * shape.chunk / (c_ms * 1e-3), 1)),
+        "chunk_attention": dict(_pcts(ca_ms), queries_per_seq=shape.chunk,
+                                kernel="large-chunk" if ca_kernel == 1 else "split",
+                                query_tokens_per_s=round(shape.batch * shape.chunk / (float(np.mean(ca_ms)) * 1e-3), 1),
+                                **_chunk_attention_rates(lens_c, shape.chunk, shape.num_q_heads,
+                                                         float(np.mean(ca_ms)))),
         "roofline": _roofline("kvq_paged_decode_attention (decode + split merge launches)", b_att, t_ms,
                               c_dec["GBps"], t_dec),
         "roofline_chunk_append": _roofline("kvq_rotate_quantize_append, 32 x 512-token chunk", b_chunk, c_ms,
@@ -1097,14 +1132,16 @@ def suite_multi_query(dev, stream, cpu):
             run(i)
         ms = _timed(run, 20, stream)
         nbytes = decode_bytes(lens, shape.num_q_heads, shape.num_kv_heads, shape.bits, shape.page_size)
-        # multiply-adds of QK and PV over the causal window of every query
-        causal = float(np.sum([qlen * (int(n) - qlen) + qlen * (qlen + 1) / 2 for n in lens]))
-        flops = 4.0 * 128 * shape.num_q_heads * causal
+        chunk = kvq.prefill_kernel(shape.batch, qlen, shape.num_q_heads, shape.num_kv_heads) == 1
+        rates = _chunk_attention_rates(lens, qlen, shape.num_q_heads, ms)
+        if not chunk:  # the split kernel's matrix-core work is not three fp16 passes
+            rates = {"attention_TFLOPs": rates["attention_TFLOPs"]}
         rows.append(_line(workload=f"{name} shape, {qlen} queries per sequence "
                                    f"({'speculative verification' if qlen < 16 else 'chunked-prefill chunk'})",
-                          batch=shape.batch, queries_per_seq=qlen, attention_ms=round(ms, 5),
-                          cache_read_GBps=round(nbytes / ms / 1e6, 1), attention_TFLOPs=round(flops / ms / 1e9, 2),
-                          query_tokens_per_s=round(shape.batch * qlen / (ms * 1e-3), 1)))
+                          batch=shape.batch, queries_per_seq=qlen,
+                          kernel="large-chunk (tiles staged per 128 columns)" if chunk else "split (16-column tiles)",
+                          attention_ms=round(ms, 5), cache_read_GBps=round(nbytes / ms / 1e6, 1),
+                          query_tokens_per_s=round(shape.batch * qlen / (ms * 1e-3), 1), **rates))
         del caches
         torch_empty_cache()
     return rows

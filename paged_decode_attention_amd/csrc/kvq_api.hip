@@ -485,6 +485,11 @@ kvq_status kvq_paged_prefill_attention(
   return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+int32_t kvq_paged_prefill_kernel(int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
+  if (batch <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return -1;
+  return kvq::chunk_attention_shape(batch, max_q_len, num_q_heads, num_kv_heads) ? 1 : 0;
+}
+
 // ---------------------------------------------------------------------------- bf16 baseline
 
 kvq_status kvq_bf16_cache_write(

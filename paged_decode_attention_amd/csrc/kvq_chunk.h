@@ -9,6 +9,8 @@ namespace kvq {
 
 // Whether kvq_paged_prefill_attention takes the large-chunk kernel for these (validated) arguments.
 bool chunk_attention_applies(const DecodeArgs& a);
+// The same rule on the sizes alone (num_q_heads a multiple of num_kv_heads, all positive).
+bool chunk_attention_shape(int64_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads);
 hipError_t launch_chunk_attention(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq

@@ -534,11 +534,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
 
 }  // namespace
 
-bool chunk_attention_applies(const DecodeArgs& a) {
-  if (!a.q_lens) return false;
-  const int64_t cols = static_cast<int64_t>(a.q_len_max) * (a.num_q_heads / a.num_kv_heads);
-  const int64_t blocks = (cols + kColsWg - 1) / kColsWg * a.num_kv_heads * a.batch;
+bool chunk_attention_shape(int64_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
+  const int64_t cols = static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads);
+  const int64_t blocks = (cols + kColsWg - 1) / kColsWg * num_kv_heads * batch;
   return cols >= kColsWg && blocks >= 256 && cols / kColsWg < 65536;
+}
+
+bool chunk_attention_applies(const DecodeArgs& a) {
+  return a.q_lens && chunk_attention_shape(a.batch, a.q_len_max, a.num_q_heads, a.num_kv_heads);
 }
 
 hipError_t launch_chunk_attention(const DecodeArgs& a, hipStream_t stream) {

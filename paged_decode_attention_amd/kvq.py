@@ -22,7 +22,7 @@ EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_rotate_quantize_append",
            "kvq_bf16_cache_write", "kvq_paged_decode_attention_bf16", "kvq_decode_step",
            "kvq_paged_prefill_workspace_size", "kvq_paged_prefill_attention", "kvq_pc_write_pages",
            "kvq_pc_decode_workspace_size", "kvq_pc_decode_attention", "kvq_paged_decode_bf16_workspace_size",
-           "kvq_paged_decode_attention_noalloc")
+           "kvq_paged_decode_attention_noalloc", "kvq_paged_prefill_kernel")
 
 
 class KVQError(RuntimeError):
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         _p, _i32, _p]
     L.kvq_dequant_page.restype = _i32
     L.kvq_dequant_page.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]
+    L.kvq_paged_prefill_kernel.restype = _i32
+    L.kvq_paged_prefill_kernel.argtypes = [_i32, _i32, _i32, _i32]
     L.kvq_paged_prefill_workspace_size.restype = _sz
     L.kvq_paged_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
     L.kvq_paged_prefill_attention.restype = _i32
@@ -302,6 +304,11 @@ def prefill_workspace_size(batch: int, max_q_len: int, num_q_heads: int, num_kv_
                            page_size: int, pages_per_split: int = 0) -> int:
     return int(lib().kvq_paged_prefill_workspace_size(batch, max_q_len, num_q_heads, num_kv_heads, HEAD_DIM,
                                                        max_context_len, page_size, pages_per_split))
+
+
+def prefill_kernel(batch: int, max_q_len: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """kvq_paged_prefill_kernel: 1 large-chunk kernel, 0 split kernel, -1 rejected sizes."""
+    return int(lib().kvq_paged_prefill_kernel(batch, max_q_len, num_q_heads, num_kv_heads))
 
 
 def paged_prefill_attention(q: torch.Tensor, q_lens: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,

@@ -24,7 +24,20 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(kvq.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert kvq.abi_version() == 2
+    assert kvq.abi_version() == 3
+
+
+def test_prefill_kernel_choice():
+    """The large-chunk kernel is chosen from 128 (query, head) columns per KV head and 256
+    workgroups of 128 columns up; other sizes take the split kernel; invalid sizes are rejected."""
+    assert kvq.prefill_kernel(32, 512, 28, 4) == 1     # OScaR chunk: 28 x 4 x 32 workgroups
+    assert kvq.prefill_kernel(2, 512, 32, 8) == 1      # 16 x 8 x 2 = 256 workgroups
+    assert kvq.prefill_kernel(1, 512, 32, 8) == 0      # 128 workgroups: too few to fill the chip
+    assert kvq.prefill_kernel(16, 4, 32, 8) == 0       # speculative verification: 16 columns
+    assert kvq.prefill_kernel(64, 31, 32, 8) == 0      # 124 columns per KV head
+    assert kvq.prefill_kernel(64, 32, 32, 8) == 1      # 128 columns, 512 workgroups
+    assert kvq.prefill_kernel(4, 512, 28, 5) == -1     # heads not a multiple
+    assert kvq.prefill_kernel(0, 512, 32, 8) == -1
 
 
 def test_status_strings():

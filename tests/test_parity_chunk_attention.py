@@ -55,12 +55,6 @@ def _gpu(shape, plan, dev, q, q_lens, lens, q_prerotated=0, softmax_scale=0.0):
     return out.cpu().numpy()
 
 
-def _blocks(shape, qmax):
-    """Workgroups of the large-chunk launch: 128 columns each, per KV head and sequence."""
-    cols = qmax * shape.group
-    return -(-cols // 128) * shape.num_kv_heads * shape.batch
-
-
 CASES = [
     # name, overrides, context lens, q_lens, max_q_len
     ("oscar_int2", dict(batch=3), (700, 600, 520), (512, 300, 513), 513),                     # INT2, g 7
@@ -74,7 +68,7 @@ CASES = [
                          ids=[f"{c[0]}-ps{c[1].get('page_size', 16)}" for c in CASES])
 def test_chunk_attention_parity(name, overrides, lens, q_lens, qmax):
     shape, plan, cache = _case(name, overrides, lens)
-    assert qmax * shape.group >= 128 and _blocks(shape, qmax) >= 256, "not a large-chunk launch"
+    assert kvq.prefill_kernel(shape.batch, qmax, shape.num_q_heads, shape.num_kv_heads) == 1, "not a large-chunk launch"
     _say(f"chunk attention {name} {overrides} lens={lens} q_lens={q_lens}")
     q = _queries(shape, qmax, seed=sum(lens) + qmax)
     ref = O.multi_query_attention(cache, q, np.array(q_lens), plan.block_table, np.array(lens), shape.num_kv_heads,
@@ -92,6 +86,7 @@ def test_chunk_attention_parity(name, overrides, lens, q_lens, qmax):
 def test_chunk_attention_prerotated_query():
     """q_prerotated = 1 with R q given equals q_prerotated = 0 with q (same launch shape)."""
     shape, plan, cache = _case("llama3_8b", dict(batch=4), (300, 280, 256, 400))
+    assert kvq.prefill_kernel(4, 256, 32, 8) == 1
     q_lens = (256, 256, 256, 256)
     q = _queries(shape, 256, seed=11)
     r = O.rotation_matrix(128, shape.hadamard_block)
@@ -111,6 +106,7 @@ def test_chunk_attention_cache_scales():
     for K when the softmax scale undoes it, so the tiles' power-of-two exponents carry the range."""
     lens = (300, 513, 256, 77)
     shape, plan, cache = _case("llama3_8b", dict(batch=4), lens)
+    assert kvq.prefill_kernel(4, 256, 32, 8) == 1
     q_lens = (256, 256, 256, 77)
     q = _queries(shape, 256, seed=12)
     base = _gpu(shape, plan, H.upload_cache(cache), q, q_lens, lens)
