@@ -96,6 +96,7 @@ KERNEL_SOURCES = {
     "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
     "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
     "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
+    "chunk_attention_kernel": ["kvq_chunk_attn.hip", "kvq_chunk.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
 }
 CALIBRATION_BYTES = 256 << 20
 TRAFFIC_TAG = "traffic-json: "
@@ -699,6 +700,11 @@ def counters_other(args, dev):
         copies = [kvq.PagedKVCache.empty(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.bits, device=dev)
                   for _ in range(4)]
         _, attend, _ = _decode_step_fns(shape, plan, copies, dev, stream)
+        # a 512-token chunk's attention over 16384 tokens per sequence (the large-chunk kernel)
+        lens_c = torch.from_numpy(np.asarray(shape.context_lens, dtype=np.int32)).to(dev)
+        qc = torch.randn((shape.batch, shape.chunk, shape.num_q_heads, 128), device=dev).to(torch.bfloat16)
+        qlc = torch.full((shape.batch,), shape.chunk, dtype=torch.int32, device=dev)
+        btc = torch.from_numpy(plan.block_table).to(dev)
 
         def run():
             for a, b, sl in full[:args.steps]:
@@ -706,7 +712,11 @@ def counters_other(args, dev):
                                            stream=stream)
             for i in range(args.steps):
                 attend(i)
-        what = f"{min(args.steps, len(full))} chunk appends of 32 x 512 tokens, then {args.steps} decodes"
+            for i in range(2):
+                kvq.paged_prefill_attention(qc, qlc, cache, btc, lens_c, max(shape.context_lens), shape.hadamard_block,
+                                            stream=stream)
+        what = (f"{min(args.steps, len(full))} chunk appends of 32 x 512 tokens, then {args.steps} decodes and "
+                f"2 attentions of a 512-token chunk")
     torch.cuda.synchronize()
     src = torch.ones(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
