@@ -209,7 +209,8 @@ kvq_status kvq_paged_decode_attention_noalloc(
  *   q_lens           int32 [batch] (device), each in [0, max_q_len]; clamped to context_lens[b].
  *   out              float32 [batch][max_q_len][num_q_heads][head_dim], un-rotated; rows with
  *                    j >= q_lens[b] are zero.
- *   workspace        at least kvq_paged_prefill_workspace_size(...) bytes (same arguments).
+ *   workspace        at least kvq_paged_prefill_workspace_size(...) bytes (same arguments); unused (may
+ *                    be NULL, 0 bytes) when kvq_paged_prefill_kernel(...) returns 1.
  *   Any number of query heads per KV head. All other arguments as for kvq_paged_decode_attention;
  *   with max_q_len = 1 and q_lens = 1 it computes the same attention.
  *   Large chunks (kvq_paged_prefill_kernel returns 1) run a kernel that stages each cache tile once

@@ -226,7 +226,8 @@ kvq_status decode_args(
     const int32_t* context_lens, int32_t max_context_len,
     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t hadamard_block, int32_t bits, float softmax_scale,
-    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, int32_t q_len_max = 0) {
+    float* out, void* workspace, size_t workspace_bytes, int32_t pages_per_split, int32_t q_len_max = 0,
+    bool uses_workspace = true) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_pages < 0 || max_context_len < 0 ||
       max_pages_per_seq < 0 || pages_per_split < 0 || q_len_max < 0)
     return KVQ_ERR_SHAPE;
@@ -257,7 +258,8 @@ kvq_status decode_args(
     return KVQ_ERR_SHAPE;
 
   const WorkspaceLayout ws = workspace_layout(plan.num_splits, batch, num_q_heads, q_len_max > 0 ? q_len_max : 1);
-  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
+  if (uses_workspace && ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned(workspace, 16)))
+    return KVQ_ERR_WORKSPACE;
 
   a = kvq::DecodeArgs{};
   a.q_len_max = q_len_max;
@@ -285,8 +287,8 @@ kvq_status decode_args(
   a.out = out;
   a.num_splits = plan.num_splits;
   a.pages_per_split = plan.pages_per_split;
-  a.ws_acc = ws.total ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
+  a.ws_acc = (uses_workspace && ws.total) ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = (uses_workspace && ws.total) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset) : nullptr;
   return KVQ_OK;
 }
 
@@ -447,6 +449,11 @@ kvq_status kvq_dequant_page(
 
 // ---------------------------------------------------------------------------- several queries
 
+int32_t kvq_paged_prefill_kernel(int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
+  if (batch <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return -1;
+  return kvq::chunk_attention_shape(batch, max_q_len, num_q_heads, num_kv_heads) ? 1 : 0;
+}
+
 size_t kvq_paged_prefill_workspace_size(int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_context_len, int32_t page_size,
                                         int32_t pages_per_split) {
@@ -471,23 +478,20 @@ kvq_status kvq_paged_prefill_attention(
     hipStream_t stream) {
   if (max_q_len <= 0) return KVQ_ERR_SHAPE;
   if (static_cast<int64_t>(batch) * max_q_len > 0x7FFFFFFF / 128) return KVQ_ERR_UNSUPPORTED;
+  // the large-chunk kernel takes no workspace (decode_args rejects the other sizes first)
+  const bool chunk = kvq_paged_prefill_kernel(batch, max_q_len, num_q_heads, num_kv_heads) == 1;
   kvq::DecodeArgs a;
   if (kvq_status s = decode_args(a, q, q_prerotated, k_codes, v_codes, k_sz, v_sz, num_pages, page_size, block_table,
                                  max_pages_per_seq, context_lens, max_context_len, batch, num_q_heads, num_kv_heads,
                                  head_dim, hadamard_block, bits, softmax_scale, out, workspace, workspace_bytes,
-                                 pages_per_split, max_q_len))
+                                 pages_per_split, max_q_len, !chunk))
     return s;
   if (batch == 0) return KVQ_OK;
   if (!q_lens) return KVQ_ERR_NULL;
   if (!aligned(q_lens, 4)) return KVQ_ERR_SHAPE;
   a.q_lens = q_lens;
-  if (kvq::chunk_attention_applies(a)) return kvq::launch_chunk_attention(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+  if (chunk) return kvq::launch_chunk_attention(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
   return kvq::launch_decode_mfma(a, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
-}
-
-int32_t kvq_paged_prefill_kernel(int32_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
-  if (batch <= 0 || max_q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads) return -1;
-  return kvq::chunk_attention_shape(batch, max_q_len, num_q_heads, num_kv_heads) ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------- bf16 baseline

@@ -333,6 +333,8 @@ def paged_prefill_attention(q: torch.Tensor, q_lens: torch.Tensor, cache: PagedK
         raise ValueError("out must be a contiguous [B, Q, Hq, 128] float32 tensor")
     need = prefill_workspace_size(bsz, qmax, hq, cache.num_kv_heads, max_context_len, cache.page_size,
                                   pages_per_split)
+    if prefill_kernel(bsz, qmax, hq, cache.num_kv_heads) == 1:
+        need = 0  # the large-chunk kernel leaves the workspace untouched
     if workspace is None and need > 0:
         workspace = _own_workspace(need, q.device, stream)
     ws_ptr, ws_bytes = _workspace(workspace)

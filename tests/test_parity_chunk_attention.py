@@ -40,12 +40,13 @@ def _queries(shape, qmax, seed):
     return W.f32_to_bf16_bits(rng.standard_normal((shape.batch, qmax, shape.num_q_heads, 128)).astype(np.float32))
 
 
-def _gpu(shape, plan, dev, q, q_lens, lens, q_prerotated=0, softmax_scale=0.0):
+def _gpu(shape, plan, dev, q, q_lens, lens, q_prerotated=0, softmax_scale=0.0, workspace=True):
     qmax = q.shape[1]
     max_len = int(max(lens))
     nbytes = kvq.prefill_workspace_size(shape.batch, qmax, shape.num_q_heads, shape.num_kv_heads, max_len,
                                         shape.page_size)
-    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+    # (the large-chunk kernel leaves it untouched: without one the binding passes a null workspace)
+    ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda") if workspace else None
     out = torch.full((shape.batch, qmax, shape.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
     kvq.paged_prefill_attention(H.to_dev_bf16(q), H.to_dev(np.asarray(q_lens, dtype=np.int32)), dev,
                                 H.to_dev(plan.block_table), H.to_dev(np.asarray(lens, dtype=np.int32)), max_len,
@@ -84,7 +85,8 @@ def test_chunk_attention_parity(name, overrides, lens, q_lens, qmax):
 
 
 def test_chunk_attention_prerotated_query():
-    """q_prerotated = 1 with R q given equals q_prerotated = 0 with q (same launch shape)."""
+    """q_prerotated = 1 with R q given equals q_prerotated = 0 with q (same launch shape); called
+    with no workspace (a null pointer through the C ABI)."""
     shape, plan, cache = _case("llama3_8b", dict(batch=4), (300, 280, 256, 400))
     assert kvq.prefill_kernel(4, 256, 32, 8) == 1
     q_lens = (256, 256, 256, 256)
@@ -95,7 +97,7 @@ def test_chunk_attention_prerotated_query():
     dev = H.upload_cache(cache)
     ref = O.multi_query_attention(cache, qr, np.array(q_lens), plan.block_table, np.array((300, 280, 256, 400)),
                                   shape.num_kv_heads, shape.hadamard_block, q_prerotated=1)
-    got = _gpu(shape, plan, dev, qr, q_lens, (300, 280, 256, 400), q_prerotated=1)
+    got = _gpu(shape, plan, dev, qr, q_lens, (300, 280, 256, 400), q_prerotated=1, workspace=False)
     worst = H.check_attention(got.reshape(-1, 128), ref.reshape(-1, 128), "prerotated")
     _say(f"  worst rel-L2 {worst:.2e}")
 
