@@ -8,6 +8,8 @@ ragged contexts whose last tile ends mid-tile (the rows past each sequence hold 
 cache's NaN poison), queries per sequence from 0 to the maximum, and a last workgroup that is
 only partly filled with columns.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -129,3 +131,93 @@ def test_chunk_attention_cache_scales():
                 worst = max(worst, H.check_attention(got[b, :ql].reshape(-1, 128), want[b, :ql].reshape(-1, 128),
                                                      f"{tensor} x 2^{e}"))
             _say(f"  worst rel-L2 against the unscaled output {worst:.2e}")
+
+
+def _random_config(i):
+    r = np.random.default_rng(9100 + i)
+    kvh = int(r.choice([4, 8]))
+    g = int(r.integers(1, 5))
+    qmax = int(r.choice([128, 160, 256]))
+    per_seq = -(-qmax * g // 128) * kvh                  # workgroups per sequence
+    b = max(2, -(-256 // per_seq))                        # at least 256 workgroups in all
+    q_lens = [int(x) for x in r.integers(1, qmax + 1, size=b)]
+    q_lens[0] = qmax
+    if b > 2:
+        q_lens[1] = 0                                     # a sequence without queries
+    lens = [ql + int(r.integers(0, 300)) for ql in q_lens]
+    lens[1] = max(lens[1], 1)
+    ps = int(r.choice([16, 32, 64]))
+    bits, ts = [(4, 0), (4, 1), (2, 0), (2, 1)][int(r.integers(0, 4))]
+    hb = int(2 ** int(r.integers(0, 8)))
+    shape = W.config("tiny", batch=b, num_q_heads=kvh * g, num_kv_heads=kvh, context_lens=tuple(lens),
+                     hadamard_block=hb, bits=bits, token_scale=ts, page_size=ps, seed=9100 + i)
+    return shape, q_lens, qmax
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_chunk_attention_random(i):
+    """Seeded random large-chunk configurations: 4 or 8 KV heads, GQA 1-4, 128-256 queries per
+    sequence (ragged, one sequence without any), contexts up to 300 tokens past the queries, pages
+    of 16/32/64, INT4/INT2 with and without the token scale, Hadamard blocks 1-128."""
+    shape, q_lens, qmax = _random_config(i)
+    assert kvq.prefill_kernel(shape.batch, qmax, shape.num_q_heads, shape.num_kv_heads) == 1
+    lens = shape.context_lens
+    _say(f"chunk random {i}: {shape.batch} seq, lens {lens}, q_lens {q_lens}, heads {shape.num_q_heads}/"
+         f"{shape.num_kv_heads}, page {shape.page_size}, INT{shape.bits}, token scale {shape.token_scale}, "
+         f"block {shape.hadamard_block}")
+    plan = W.plan_pages(shape, extra_tokens=0)
+    seq, pos = W.prefill_order(shape)
+    k, v = W.draw_kv(shape, len(seq))
+    cache = O.PagedCache(plan.num_pages, shape.num_kv_heads, shape.page_size, shape.head_dim, shape.bits)
+    O.append(cache, k, v, W.slots_for_positions(plan, shape.page_size, seq, pos), shape.hadamard_block,
+             shape.token_scale)
+    q = _queries(shape, qmax, seed=9100 + i)
+    ref = O.multi_query_attention(cache, q, np.array(q_lens), plan.block_table, np.array(lens), shape.num_kv_heads,
+                                  shape.hadamard_block)
+    got = _gpu(shape, plan, H.upload_cache(cache), q, q_lens, lens)
+    assert np.all(np.isfinite(got))
+    worst = 0.0
+    for b, ql in enumerate(q_lens):
+        assert np.all(got[b, ql:] == 0)
+        if ql:
+            worst = max(worst, H.check_attention(got[b, :ql].reshape(-1, 128), ref[b, :ql].reshape(-1, 128),
+                                                 f"random {i} b{b}"))
+    _say(f"  worst rel-L2 {worst:.2e}")
+
+
+def test_chunk_attention_skips_invalid_pages():
+    """Page-table entries outside [0, num_pages) are skipped: the attention equals the oracle's over
+    the sequence with those pages' tokens left out (built from the oracle's gather and attend)."""
+    lens = (300, 600, 280, 400)
+    shape, plan, cache = _case("llama3_8b", dict(batch=4), lens)
+    q_lens = (256, 256, 256, 200)
+    assert kvq.prefill_kernel(4, 256, 32, 8) == 1
+    bt = plan.block_table.copy()
+    dropped = {0: [3, 7], 1: [1, 20, 30]}                 # (sequence: page indices) made invalid
+    for b, pages in dropped.items():
+        for j, p in enumerate(pages):
+            bt[b, p] = -1 if j % 2 == 0 else plan.num_pages + 5
+    q = _queries(shape, 256, seed=13)
+    _say("chunk attention with invalid page ids")
+    got = _gpu(shape, dataclasses.replace(plan, block_table=bt), H.upload_cache(cache), q, q_lens, lens)
+    assert np.all(np.isfinite(got))
+    g = shape.group
+    r = O.rotation_matrix(128, shape.hadamard_block)
+    scale = 1.0 / np.sqrt(128.0)
+    rng = np.random.default_rng(3)
+    for b in (0, 1, 2):
+        ps = shape.page_size
+        keep = np.ones(lens[b], dtype=bool)
+        for p in dropped.get(b, []):
+            keep[p * ps:(p + 1) * ps] = False
+        for kvh in range(shape.num_kv_heads):
+            kh, vh = O.gather_sequence(cache, plan.block_table[b], lens[b], kvh)
+            for j in sorted(rng.choice(q_lens[b], 24, replace=False)):
+                n = lens[b] - q_lens[b] + j + 1
+                sel = keep[:n]
+                for hh in range(g):
+                    h = kvh * g + hh
+                    qq = r @ O.bf16_to_f32(q[b, j, h]).astype(np.float64)
+                    want = r.T @ O.attend(qq, kh[:n][sel], vh[:n][sel], scale)
+                    e = H.rel_l2(got[b, j, h], want)
+                    assert e <= H.ATTN_RTOL, (b, j, h, float(e))
