@@ -151,10 +151,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int G = lane >> 4;
   const int n = lane & 15;
-  const int kvh = static_cast<int>(blockIdx.y);
-  const int b = static_cast<int>(blockIdx.z);
-  const int c0 = kColsWg * static_cast<int>(blockIdx.x);
   const int g = a.num_q_heads / a.num_kv_heads;
+  // Workgroups go to the eight XCDs in turn. With a multiple of eight, workgroup w takes the logical
+  // block (w % 8) (n / 8) + w / 8, so each XCD runs consecutive column blocks of the same
+  // (sequence, KV head) items at the same time and their tiles are read once into its L2.
+  const uint32_t n_cb = static_cast<uint32_t>((a.q_len_max * g + kColsWg - 1) / kColsWg);
+  const uint32_t n_wg = gridDim.x;
+  const uint32_t wg = (n_wg % 8 == 0) ? (blockIdx.x % 8) * (n_wg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const uint32_t item = wg / n_cb;
+  const int kvh = static_cast<int>(item % static_cast<uint32_t>(a.num_kv_heads));
+  const int b = static_cast<int>(item / static_cast<uint32_t>(a.num_kv_heads));
+  const int c0 = kColsWg * static_cast<int>(wg % n_cb);
   const int ps = a.page_size;
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int qlen = min(min(max(ro_load(a.q_lens, b), 0), a.q_len_max), len);
@@ -537,7 +544,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
 bool chunk_attention_shape(int64_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
   const int64_t cols = static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads);
   const int64_t blocks = (cols + kColsWg - 1) / kColsWg * num_kv_heads * batch;
-  return cols >= kColsWg && blocks >= 256 && cols / kColsWg < 65536;
+  return cols >= kColsWg && blocks >= 256 && blocks * 64 * kWaves < (int64_t{1} << 31);
 }
 
 bool chunk_attention_applies(const DecodeArgs& a) {
@@ -546,8 +553,8 @@ bool chunk_attention_applies(const DecodeArgs& a) {
 
 hipError_t launch_chunk_attention(const DecodeArgs& a, hipStream_t stream) {
   const int64_t cols = static_cast<int64_t>(a.q_len_max) * (a.num_q_heads / a.num_kv_heads);
-  const dim3 grid(static_cast<unsigned>((cols + kColsWg - 1) / kColsWg), static_cast<unsigned>(a.num_kv_heads),
-                  static_cast<unsigned>(a.batch));
+  const int64_t n_wg = (cols + kColsWg - 1) / kColsWg * a.num_kv_heads * a.batch;  // < 2^31: checked by the caller
+  const dim3 grid(static_cast<unsigned>(n_wg));
   if (a.bits == 4) hipLaunchKernelGGL(chunk_attention_kernel<4>, grid, dim3(64 * kWaves), 0, stream, a);
   else hipLaunchKernelGGL(chunk_attention_kernel<2>, grid, dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
