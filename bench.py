@@ -110,7 +110,9 @@ def sources_sha256(kernel: str) -> str:
         with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
             h.update(fh.read())
     tu = KERNEL_SOURCES[kernel][0]
-    h.update(" ".join(_build.CFLAGS + _build.EXTRA_CFLAGS.get(tu, [])).encode())
+    # the flags without the include directory (an absolute path that differs between checkouts)
+    flags = [f for f in _build.CFLAGS + _build.EXTRA_CFLAGS.get(tu, []) if not os.path.isabs(f)]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 
