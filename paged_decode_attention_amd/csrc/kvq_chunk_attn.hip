@@ -48,6 +48,7 @@ static_assert(kColsWg * kQStride * 4 <= 2 * kBufBytes, "the staged query fits th
 static_assert(kColsWg * kOStride * 4 <= 2 * kBufBytes, "the output rows fit the tile buffers");
 constexpr float kLazy = 8.0f;                 // rescale when the maximum grows by more than 2^8
 constexpr float kNoMag = -1000.0f;            // V exponent before any nonzero V
+constexpr _Float16 kOne16 = static_cast<_Float16>(1.0f);
 
 // Exponent e with |x| 2^-e in [2^13, 2^14) for the largest magnitude x of a block (0 for an empty
 // or non-finite block), clamped so that 2^-e stays a normal float.
@@ -170,7 +171,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   auto col_row = [&](int c) -> int64_t {
     return (static_cast<int64_t>(b) * a.q_len_max + c / g) * a.num_q_heads + static_cast<int64_t>(kvh) * g + c % g;
   };
-  const LaneFwht lf = lane_fwht(a.rot, n);
 
   if (c0 >= valid_cols) {  // no query in this workgroup: its rows of out are zero
     for (int cl = 4 * w + G; cl < kColsWg; cl += 4 * kWaves) {
@@ -219,6 +219,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
     if (c < valid_cols) bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.q + col_row(c) * kHeadDim + 8 * n), x);
     int pos = n;
     if (!a.q_prerotated) {
+      const LaneFwht lf = lane_fwht(a.rot, n);
       fwht_row16_planned(x, a.rot, lf);
       pos = lf.pos;
     }
@@ -354,7 +355,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[cb][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf};
+  // Running maximum per column, kept as nbase = -(reference maximum) (0 before the first score)
+  // and the threshold thr on a step's maximum relative to it above which the reference is raised:
+  // -inf before the first score (any finite score raises it), kLazy after.
+  float nbase[2] = {0.f, 0.f};
+  float thr[2] = {kNegInf, kNegInf};
   float l_part[2] = {0.f, 0.f};
   float e_acc = kNoMag;  // V exponent E the accumulators are kept in (uniform)
 
@@ -388,9 +393,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
     // P = 2^x in fp16 and O^T += V^T P.
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      float m_ref[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) m_ref[cb] = (m_run[cb] == kNegInf) ? 0.f : m_run[cb];
       float x[2][2][4];  // [cb][block of the step][r]
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -410,9 +412,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
           for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qhi[cb][ks], d, 0, 0, 0);
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qlo[cb][ks], d, 0, 0, 0);
-          const float base = -m_ref[cb];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[cb][u][r] = __builtin_fmaf(d[r], km[r], __builtin_fmaf(kz[r], qsum[cb], base));
+          for (int r = 0; r < 4; ++r) x[cb][u][r] = __builtin_fmaf(d[r], km[r], __builtin_fmaf(kz[r], qsum[cb], nbase[cb]));
         }
       }
 
@@ -438,11 +439,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
 #pragma unroll
           for (int r = 0; r < 4; ++r) mt = fmaxf(mt, x[cb][u][r]);
         mt = max_over_rows(mt);
-        const bool raise = (m_run[cb] == kNegInf) ? (mt != kNegInf) : (mt > kLazy);
+        const bool raise = !(mt <= thr[cb]);
         if (__any(raise)) {
           const float dm = raise ? mt : 0.f;
-          const float alpha = (m_run[cb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(-dm);
-          m_run[cb] = raise ? m_ref[cb] + mt : m_run[cb];
+          const float alpha = (thr[cb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(-dm);
+          nbase[cb] -= dm;
+          thr[cb] = raise ? kLazy : thr[cb];
           l_part[cb] *= alpha;
 #pragma unroll
           for (int m = 0; m < 8; ++m) acc[cb][m] *= alpha;
@@ -455,14 +457,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[u][r] = __builtin_amdgcn_exp2f(x[cb][u][r]);
-            l_part[cb] += p[u][r];
-          }
+          for (int r = 0; r < 4; ++r) p[u][r] = __builtin_amdgcn_exp2f(x[cb][u][r]);
         pf[cb] = v8h{static_cast<_Float16>(p[0][0]), static_cast<_Float16>(p[0][1]),
                      static_cast<_Float16>(p[0][2]), static_cast<_Float16>(p[0][3]),
                      static_cast<_Float16>(p[1][0]), static_cast<_Float16>(p[1][1]),
                      static_cast<_Float16>(p[1][2]), static_cast<_Float16>(p[1][3])};
+        // the row sum takes the fp16 weights the products use, two per dot instruction (fp32 sum)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          l_part[cb] = __builtin_amdgcn_fdot2(h2{pf[cb][2 * k], pf[cb][2 * k + 1]}, h2{kOne16, kOne16}, l_part[cb], false);
       }
 
       // O^T += V^T P: 16-channel block m of this 32-token step
@@ -477,26 +480,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
     }
   };
 
-  // ---- the walk: tile i computes from buffer i & 1 while tile i + 2 loads; then tile i + 1 is
-  // staged in the other buffer, with E from the V exponents its waves published a tile earlier,
-  // and tile i + 2's are published (the loop is not unrolled: the tile step is a large block of
-  // code, and instruction fetch matters).
+  // ---- the walk: tile i + 1 is staged in the buffer the previous step has released, with E from
+  // the V exponents its waves published a tile earlier; tile i + 2's loads are issued, tile i
+  // computes from buffer i & 1, and tile i + 2's exponents are published. Staging before the
+  // compute leaves only one tile of loads in registers across it. (The loop is not unrolled: the
+  // tile step is a large block of code, and instruction fetch matters.)
   auto tile_exponent = [&](int i, float e_prev) {
     const float* ve = vexp[i % 3];
     return fmaxf(e_prev, fmaxf(fmaxf(ve[0], ve[1]), fmaxf(ve[2], ve[3])));
   };
-  float e_cur = tile_exponent(0, kNoMag);
-  stage(0, ta, ok_a, 0, e_cur);
+  float e_stg = tile_exponent(0, kNoMag);  // E of the last staged tile
+  stage(0, ta, ok_a, 0, e_stg);
   __syncthreads();
 #pragma unroll 1
   for (int i = 0;; ++i) {
+    const float e_tile = e_stg;
+    if (i + 1 < n_tiles) {
+      e_stg = tile_exponent(i + 1, e_stg);
+      stage(i + 1, tb_, ok_b, (i + 1) & 1, e_stg);
+    }
     SubTile tc = {};
     bool ok_c = false;
     if (i + 2 < n_tiles) tc = fetch(i + 2, ok_c);
-    compute(i, i & 1, e_cur);
+    compute(i, i & 1, e_tile);
     if (i + 1 >= n_tiles) break;
-    e_cur = tile_exponent(i + 1, e_cur);
-    stage(i + 1, tb_, ok_b, (i + 1) & 1, e_cur);
     if (i + 2 < n_tiles) publish(i + 2, tc, ok_c);
     __syncthreads();
     tb_ = tc;
@@ -511,6 +518,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   }
   __syncthreads();  // every wave is done with the tile buffers
   float* const os = reinterpret_cast<float*>(lds);
+  // the lane's transform plan, rebuilt from the lane id rather than kept in registers over the walk
+  const LaneFwht lf_out = lane_fwht(a.rot, static_cast<int>(__lane_id()) & 15);
   const float ev_scale = (e_acc == kNoMag) ? 0.f : ldexpf(1.f, static_cast<int>(e_acc));
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -530,9 +539,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
     const float4 xa = *reinterpret_cast<const float4*>(os + cl * kOStride + 8 * n);
     const float4 xb = *reinterpret_cast<const float4*>(os + cl * kOStride + 8 * n + 4);
     float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    fwht_row16_planned(x, a.rot, lf);  // R^T = R: back to the original basis
+    fwht_row16_planned(x, a.rot, lf_out);  // R^T = R: back to the original basis
     if (c < rows_cols) {
-      float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf.pos);
+      float4* dst = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * lf_out.pos);
       dst[0] = make_float4(x[0], x[1], x[2], x[3]);
       dst[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
