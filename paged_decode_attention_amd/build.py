@@ -43,9 +43,12 @@ CFLAGS = [
 
 
 # Per-source extras. The write path never sees a NaN it must order (its min / max run on finite
-# rotated values), so NaN-honouring min / max lowering - a canonicalising move that keeps the DPP
-# row reductions from fusing into single instructions - is switched off there.
-EXTRA_CFLAGS = {"kvq_append.hip": ["-fno-honor-nans"], "kvq_pc_write.hip": ["-fno-honor-nans"]}
+# rotated values), and neither does the large-chunk attention (its maxima run on scores that are
+# finite or -inf: rows past a sequence and tokens on invalid pages get zero scale and zero), so
+# NaN-honouring min / max lowering - a canonicalising move that keeps the DPP row reductions from
+# fusing into single instructions - is switched off there.
+EXTRA_CFLAGS = {"kvq_append.hip": ["-fno-honor-nans"], "kvq_pc_write.hip": ["-fno-honor-nans"],
+                "kvq_chunk_attn.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:

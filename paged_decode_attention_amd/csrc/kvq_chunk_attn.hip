@@ -438,9 +438,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mt = fmaxf(mt, x[cb][u][r]);
-        mt = max_over_rows(mt);
-        const bool raise = !(mt <= thr[cb]);
-        if (__any(raise)) {
+        // Only a step whose scores pass the threshold somewhere needs the column maxima (over the
+        // four row groups, so that a column's lanes agree); most steps skip that reduction.
+        if (__any(!(mt <= thr[cb]))) {
+          mt = max_over_rows(mt);
+          const bool raise = !(mt <= thr[cb]);
           const float dm = raise ? mt : 0.f;
           const float alpha = (thr[cb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(-dm);
           nbase[cb] -= dm;
