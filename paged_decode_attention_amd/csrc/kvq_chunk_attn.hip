@@ -430,20 +430,24 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
             }
       }
 
-      v8h pf[2];
+      // Step maxima per lane. Only a step whose scores pass the rescale threshold somewhere needs
+      // the column maxima (over the four row groups, so that a column's lanes agree); most steps
+      // skip that reduction and the rescale, for both column blocks in one branch.
+      float mt[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        float mt = kNegInf;
+        mt[cb] = kNegInf;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mt = fmaxf(mt, x[cb][u][r]);
-        // Only a step whose scores pass the threshold somewhere needs the column maxima (over the
-        // four row groups, so that a column's lanes agree); most steps skip that reduction.
-        if (__any(!(mt <= thr[cb]))) {
-          mt = max_over_rows(mt);
-          const bool raise = !(mt <= thr[cb]);
-          const float dm = raise ? mt : 0.f;
+          for (int r = 0; r < 4; ++r) mt[cb] = fmaxf(mt[cb], x[cb][u][r]);
+      }
+      if (__any(!(mt[0] <= thr[0]) || !(mt[1] <= thr[1]))) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const float mc = max_over_rows(mt[cb]);
+          const bool raise = !(mc <= thr[cb]);
+          const float dm = raise ? mc : 0.f;
           const float alpha = (thr[cb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(-dm);
           nbase[cb] -= dm;
           thr[cb] = raise ? kLazy : thr[cb];
@@ -455,6 +459,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[cb][u][r] -= dm;
         }
+      }
+      v8h pf[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
         float p[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
