@@ -36,9 +36,9 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kColsWave = 32;                 // two 16-column blocks per wave
 constexpr int kColsWg = kColsWave * kWaves;   // 128
-constexpr int kTile = 64;                     // tokens per tile: one 16-token sub-tile per wave
+constexpr int kTile = 16 * kWaves;            // tokens per tile: one 16-token sub-tile per wave
 constexpr int kKStride = 136;                 // halves per K row in LDS (272 B: 16 rows hit distinct banks)
-constexpr int kVStride = 72;                  // halves per V^T row (144 B)
+constexpr int kVStride = kTile + 8;           // halves per V^T row (the tile plus 16 B)
 constexpr int kKBytes = kTile * kKStride * 2;
 constexpr int kVBytes = kHeadDim * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;  // one tile: 35,840 B; two buffers
@@ -140,7 +140,7 @@ __device__ __forceinline__ int vt_swizzle(int ch, int pos) {
 }
 
 template <int BITS>
-__global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kernel(const DecodeArgs a) {
   constexpr int kQmax = (1 << BITS) - 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
   __shared__ __attribute__((aligned(16))) float2 mz[2][kTile];  // per K token: (scale 2^eQ, zero)
@@ -233,7 +233,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   am = wave_max(am);
   if (lane == 0) qmax_w[w] = am;
   __syncthreads();
-  const int eq = block_exponent(fmaxf(fmaxf(qmax_w[0], qmax_w[1]), fmaxf(qmax_w[2], qmax_w[3])));
+  float qm = qmax_w[0];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) qm = fmaxf(qm, qmax_w[v]);
+  const int eq = block_exponent(qm);
   const float sq = ldexpf(1.f, -eq);
   v8h qhi[2][4], qlo[2][4];
   float qsum[2];
@@ -367,9 +370,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   auto compute = [&](int i, int buf, float e_tile) {
     const uint8_t* const kb = lds + buf * kBufBytes;
     const uint8_t* const vb = kb + kKBytes;
-    bool pok[4], all_ok = true;
+    bool pok[kWaves], all_ok = true;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < kWaves; ++t) {
       pok[t] = pvalid[buf][t] != 0.f;
       all_ok = all_ok && pok[t];
     }
@@ -386,13 +389,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
       e_acc = e_tile;
     }
 
-    // Two 32-token steps. Scores of 16-token blocks t = 2 st, 2 st + 1 x 16-column block cb: q . c
+    // 32-token steps. Scores of 16-token blocks t = 2 st, 2 st + 1 x 16-column block cb: q . c
     // on the matrix cores (hi and lo query parts, four 32-channel steps each), then
     // x = scale (q . c) + zero sum(q) - m with the running maximum (row group G holds tokens
     // 16 t + 4 G + r of lane n's column), the maximum raised when the step's exceeds it by kLazy,
     // P = 2^x in fp16 and O^T += V^T P.
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < kTile / 32; ++st) {
       float x[2][2][4];  // [cb][block of the step][r]
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -497,7 +500,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void chunk_attention_kernel(const D
   // tile step is a large block of code, and instruction fetch matters.)
   auto tile_exponent = [&](int i, float e_prev) {
     const float* ve = vexp[i % 3];
-    return fmaxf(e_prev, fmaxf(fmaxf(ve[0], ve[1]), fmaxf(ve[2], ve[3])));
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) e_prev = fmaxf(e_prev, ve[v]);
+    return e_prev;
   };
   float e_stg = tile_exponent(0, kNoMag);  // E of the last staged tile
   stage(0, ta, ok_a, 0, e_stg);
