@@ -394,30 +394,45 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
     // x = scale (q . c) + zero sum(q) - m with the running maximum (row group G holds tokens
     // 16 t + 4 G + r of lane n's column), the maximum raised when the step's exceeds it by kLazy,
     // P = 2^x in fp16 and O^T += V^T P.
+    // q . c of one step on the matrix cores: d[cb][u] for 16-token block 2 st + u
+    auto qk = [&](int st, v4f (&d)[2][2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const _Float16* krow = reinterpret_cast<const _Float16*>(kb) + (16 * (2 * st + u) + n) * kKStride + 8 * G;
+        v8h kf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const v8h*>(krow + 32 * ks);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          v4f e = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qhi[cb][ks], e, 0, 0, 0);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) e = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qlo[cb][ks], e, 0, 0, 0);
+          d[cb][u] = e;
+        }
+      }
+    };
+    // The next step's products are issued before this step's softmax: the matrix cores work on
+    // them while the vector units run the softmax.
+    v4f dq[kTile / 32][2][2];
+    qk(0, dq[0]);
 #pragma unroll
     for (int st = 0; st < kTile / 32; ++st) {
+      if (st + 1 < kTile / 32) qk(st + 1, dq[st + 1]);
       float x[2][2][4];  // [cb][block of the step][r]
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int t = 2 * st + u;
-        const _Float16* krow = reinterpret_cast<const _Float16*>(kb) + (16 * t + n) * kKStride + 8 * G;
-        v8h kf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const v8h*>(krow + 32 * ks);
         const float4 u0 = *reinterpret_cast<const float4*>(&mz[buf][16 * t + 4 * G]);
         const float4 u1 = *reinterpret_cast<const float4*>(&mz[buf][16 * t + 4 * G + 2]);
         const float km[4] = {u0.x, u0.z, u1.x, u1.z};
         const float kz[4] = {u0.y, u0.w, u1.y, u1.w};
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qhi[cb][ks], d, 0, 0, 0);
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qlo[cb][ks], d, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[cb][u][r] = __builtin_fmaf(d[r], km[r], __builtin_fmaf(kz[r], qsum[cb], nbase[cb]));
-        }
+          for (int r = 0; r < 4; ++r)
+            x[cb][u][r] = __builtin_fmaf(dq[st][cb][u][r], km[r], __builtin_fmaf(kz[r], qsum[cb], nbase[cb]));
       }
 
       if (!full) {  // tokens past a column's causal limit or on an invalid page
