@@ -11,6 +11,10 @@
 - The OScaR INT2 chunked prefill (32 x 16384 tokens, 512-token chunks landing mid-page) through
   the GPU append, call by call as the benchmark issues it, against the oracle's placement of
   every token: the whole cache, byte by byte.
+- The attention of a 512-token chunk over the OScaR cache (32 x 16384 tokens, 28/4 heads, every
+  sequence with 512 queries: the large-chunk kernel's full grid): the oracle caches three whole
+  sequences, and every head of ten query rows of each (the first two, the middle one, the last
+  two and five more) is compared; the whole output must be finite.
 
 Each case prints its name before it touches the GPU.
 """
@@ -134,3 +138,43 @@ def test_append_full_oscar_chunked_prefill():
     slots = np.concatenate(slot_list)
     ref, diag = H.host_cache_from_oracle(k, v, slots, plan.num_pages, ps, hb, shape.bits, ts)
     compare_caches(got, ref, [(slots, _t_diag(diag))], "oscar_int2 chunked prefill")
+
+
+@pytest.mark.timeout(600)
+def test_chunk_attention_full_oscar():
+    shape = W.config("oscar_int2")
+    ps, hb = shape.page_size, shape.hadamard_block
+    lens = np.asarray(shape.context_lens, dtype=np.int64)
+    qmax = shape.chunk
+    picked = [0, 13, 31]
+    assert kvq.prefill_kernel(shape.batch, qmax, shape.num_q_heads, shape.num_kv_heads) == 1
+    _say(f"chunk attention full oscar_int2: {shape.batch} x {qmax} queries x {shape.num_q_heads} heads over "
+         f"{int(lens.max())} tokens; oracle sequences {picked}")
+    plan = W.plan_pages(shape, extra_tokens=1)
+    seq, pos = W.prefill_order(shape)
+    keep = np.isin(seq, picked)
+    k, v = W.draw_kv(shape, int(keep.sum()))
+    slots = W.slots_for_positions(plan, ps, seq[keep], pos[keep])
+    cache, _ = H.host_cache_from_oracle(k, v, slots, plan.num_pages, ps, hb, shape.bits, shape.token_scale)
+    del k, v
+    # the other sequences' pages hold zero scale and zero: finite outputs that nothing checks
+    for a in (cache.k_sz, cache.v_sz):
+        a[np.isnan(a)] = 0.0
+    rng = np.random.default_rng(shape.seed + 77)
+    q = W.f32_to_bf16_bits(rng.standard_normal((shape.batch, qmax, shape.num_q_heads, 128), dtype=np.float32))
+    r = np.random.default_rng(5120)
+    js = sorted({0, 1, qmax // 2, qmax - 2, qmax - 1, *r.choice(qmax, 5, replace=False).tolist()})
+    rows = [(b, j, h) for b in picked for h in range(shape.num_q_heads) for j in js]  # one gather per KV head
+    q_lens = np.full(shape.batch, qmax, dtype=np.int32)
+    ref = O.multi_query_attention(cache, q, q_lens, plan.block_table, lens, shape.num_kv_heads, hb, rows=rows)
+    out = kvq.paged_prefill_attention(H.to_dev_bf16(q), H.to_dev(q_lens), H.upload_cache(cache),
+                                      H.to_dev(plan.block_table), H.to_dev(lens.astype(np.int32)), int(lens.max()),
+                                      hb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got)), "non-finite attention output"
+    worst = 0.0
+    for b in picked:
+        worst = max(worst, H.check_attention(got[b, js].reshape(-1, 128), ref[b, js].reshape(-1, 128),
+                                             f"chunk attention full oscar_int2 b{b}"))
+    _say(f"  {len(rows)} rows, worst rel-L2 {worst:.2e}")
