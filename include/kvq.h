@@ -214,7 +214,7 @@ kvq_status kvq_paged_decode_attention_noalloc(
  *   Any number of query heads per KV head. All other arguments as for kvq_paged_decode_attention;
  *   with max_q_len = 1 and q_lens = 1 it computes the same attention.
  *   Large chunks (kvq_paged_prefill_kernel returns 1) run a kernel that stages each cache tile once
- *   per 128 (query, head) columns and takes both products on the fp16 matrix cores: the codes and
+ *   per 256 (query, head) columns and takes both products on the fp16 matrix cores: the codes and
  *   the query (split into fp16 hi + lo parts) exactly enough for logits of hundreds of log2 units,
  *   V and the softmax weights in fp16 (relative error about 2^-12 each); it splits no context and
  *   leaves the workspace untouched.
@@ -237,7 +237,7 @@ kvq_status kvq_paged_prefill_attention(
 /*
  * Which kernel kvq_paged_prefill_attention runs for these sizes: 1 for the large-chunk kernel -
  * max_q_len * (num_q_heads / num_kv_heads) >= 128 (query, head) columns per KV head and at least
- * 256 workgroups of 128 columns over the batch and KV heads - 0 for the split kernel of the
+ * 256 blocks of 128 columns over the batch and KV heads - 0 for the split kernel of the
  * decode with 16-column query tiles, -1 for sizes the call rejects (a size not positive,
  * num_q_heads not a multiple of num_kv_heads). Host only, no GPU call.
  */

@@ -1,6 +1,6 @@
 // Launch interface of the large-chunk attention (kvq_chunk_attn.hip): several queries per sequence
 // with at least 128 (query, head) columns per KV head, and enough of them to fill the chip - one
-// launch, each cache tile dequantized once per 128 columns, no split partials, no workspace.
+// launch, each cache tile dequantized once per 256 columns, no split partials, no workspace.
 #pragma once
 
 #include "kvq_launch.h"

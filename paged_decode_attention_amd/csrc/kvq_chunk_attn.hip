@@ -1,25 +1,27 @@
 // Several queries per sequence, large chunks (chunked prefill): the causal attention of a
 // sequence's last q_len tokens over its paged low-bit cache, with every cache tile staged once per
-// workgroup in LDS and shared by the workgroup's 128 (query, head) columns (the paged low-bit
+// workgroup in LDS and shared by the workgroup's 256 (query, head) columns (the paged low-bit
 // attention of the OSCAR abstract on thelatestinai.com, with dequantization fused into the
 // attention as in ainews.cool "Technical Deep Dive", phase 3).
 //
-// A workgroup of four waves takes 128 columns of one (sequence, KV head) item - column c is
-// query c / g, head c % g - and walks the sequence in 64-token tiles. Each wave loads one 16-token
-// sub-tile (K and V codes, scale/zero) a tile ahead and stages it in LDS:
+// A workgroup of eight waves takes 256 columns of one (sequence, KV head) item - column c is
+// query c / g, head c % g - and walks the sequence in 64-token tiles. Each of the first four waves
+// loads one 16-token sub-tile (K and V codes, scale/zero) a tile ahead and stages it in LDS; the
+// other four only compute, so on each SIMD one wave starts its matrix work on a tile while the
+// other still stages the next one:
 //   K: the codes themselves as fp16 integers (exact), token-major, with each token's scale and zero
 //      beside them;
 //   V: dequantized to fp16 (d c + z, rounded once), channel-major, scaled by a power of two E that
 //      only grows along the walk: the largest of the V magnitudes seen so far, this tile's
 //      included (each wave publishes its sub-tile's a tile ahead), sits in [2^13, 2^14).
-// Every wave then computes, for its 32 columns, on the matrix cores (v_mfma_f32_16x16x32_f16):
+// Every wave computes, for its 32 columns, on the matrix cores (v_mfma_f32_16x16x32_f16):
 //   score = scale_j (q . c_j) + zero_j sum(q)
 // with q split into fp16 hi + lo parts (two passes, about 22 significant bits: with the long-tailed
 // token norms of the OScaR workload, logits reach hundreds of log2 units, and fp16 alone would move
 // the weights of near-tied tokens), the zero term in fp32; then the base-2 online softmax with a
 // lazy maximum, and O^T += V^T P with P in fp16; the accumulators are scaled down when E grows.
 // At the end each column is normalised, rotated back (the Hadamard transform is its own inverse)
-// and stored. No workspace, no split of the context: a workgroup per 128 columns per item already
+// and stored. No workspace, no split of the context: a workgroup per 256 columns per item already
 // fills the chip many times over for a large chunk.
 #include <algorithm>
 
@@ -33,9 +35,12 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                     // waves that stage the tiles (a 16-token sub-tile each)
+constexpr int kGroups = 2;                    // groups of kWaves waves computing on the same tiles
+constexpr int kWavesWg = kWaves * kGroups;
 constexpr int kColsWave = 32;                 // two 16-column blocks per wave
-constexpr int kColsWg = kColsWave * kWaves;   // 128
+constexpr int kColsWg = kColsWave * kWavesWg; // 256
+constexpr int kColsSel = 128;                 // the unit of the large-chunk selection rule
 constexpr int kTile = 16 * kWaves;            // tokens per tile: one 16-token sub-tile per wave
 constexpr int kKStride = 136;                 // halves per K row in LDS (272 B: 16 rows hit distinct banks)
 constexpr int kVStride = kTile + 8;           // halves per V^T row (the tile plus 16 B)
@@ -44,8 +49,8 @@ constexpr int kVBytes = kHeadDim * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;  // one tile: 35,840 B; two buffers
 constexpr int kQStride = 132;                 // floats per staged query row (prologue)
 constexpr int kOStride = 132;                 // floats per output row (epilogue)
-static_assert(kColsWg * kQStride * 4 <= 2 * kBufBytes, "the staged query fits the tile buffers");
-static_assert(kColsWg * kOStride * 4 <= 2 * kBufBytes, "the output rows fit the tile buffers");
+constexpr int kLdsBytes = (kColsWg * kQStride * 4 > 2 * kBufBytes) ? kColsWg * kQStride * 4 : 2 * kBufBytes;
+static_assert(kColsWg * kOStride * 4 <= kLdsBytes, "the output rows fit");
 constexpr float kLazy = 8.0f;                 // rescale when the maximum grows by more than 2^8
 constexpr float kNoMag = -1000.0f;            // V exponent before any nonzero V
 constexpr _Float16 kOne16 = static_cast<_Float16>(1.0f);
@@ -140,16 +145,17 @@ __device__ __forceinline__ int vt_swizzle(int ch, int pos) {
 }
 
 template <int BITS>
-__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWavesWg, 1) void chunk_attention_kernel(const DecodeArgs a) {
   constexpr int kQmax = (1 << BITS) - 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   __shared__ __attribute__((aligned(16))) float2 mz[2][kTile];  // per K token: (scale 2^eQ, zero)
   __shared__ float pvalid[2][kWaves];     // per buffer and sub-tile: page valid
   __shared__ float vexp[3][kWaves];       // per tile (mod 3) and sub-tile: V exponent, published ahead
-  __shared__ float qmax_w[kWaves];
+  __shared__ float qmax_w[kWavesWg];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const bool stager = w < kWaves;
   const int G = lane >> 4;
   const int n = lane & 15;
   const int g = a.num_q_heads / a.num_kv_heads;
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
   };
 
   if (c0 >= valid_cols) {  // no query in this workgroup: its rows of out are zero
-    for (int cl = 4 * w + G; cl < kColsWg; cl += 4 * kWaves) {
+    for (int cl = 4 * w + G; cl < kColsWg; cl += 4 * kWavesWg) {
       const int c = c0 + cl;
       if (c < rows_cols) {
         float4* o = reinterpret_cast<float4*>(a.out + col_row(c) * kHeadDim + 8 * n);
@@ -204,7 +210,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
     return load_subtile<BITS>(a, row0, ok, lane);
   };
   bool ok_a = false, ok_b = false;
-  SubTile ta = fetch(0, ok_a);
+  SubTile ta = {};
+  if (stager) ta = fetch(0, ok_a);
 
   // ---- query: rotated (R q) and times softmax_scale * log2(e), staged as fp32 rows (buffer area,
   // K-row channel order), with the workgroup's largest magnitude; then split into fp16 hi + lo
@@ -235,7 +242,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
   __syncthreads();
   float qm = qmax_w[0];
 #pragma unroll
-  for (int v = 1; v < kWaves; ++v) qm = fmaxf(qm, qmax_w[v]);
+  for (int v = 1; v < kWavesWg; ++v) qm = fmaxf(qm, qmax_w[v]);
   const int eq = block_exponent(qm);
   const float sq = ldexpf(1.f, -eq);
   v8h qhi[2][4], qlo[2][4];
@@ -265,7 +272,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
     lim[cb] = (c0 + cl < valid_cols) ? len - qlen + (c0 + cl) / g : -1;
   }
   const float k_mul = ldexpf(1.f, eq);  // the fp16 query is q 2^-eQ
-  SubTile tb_ = (n_tiles > 1) ? fetch(1, ok_b) : ta;
+  SubTile tb_ = ta;
+  if (stager && n_tiles > 1) tb_ = fetch(1, ok_b);
 
   // ---- publish the V exponent of this wave's sub-tile of tile i: the largest magnitude of its
   // dequantized values (rows past the sequence excluded)
@@ -275,8 +283,10 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
     const float mv = wave_max(fmaxf(fabsf(vz), fabsf(__builtin_fmaf(static_cast<float>(kQmax), vd, vz))));
     if (lane == 0) vexp[i % 3][w] = (mv > 0.f) ? static_cast<float>(block_exponent(mv)) : kNoMag;
   };
-  publish(0, ta, ok_a);
-  if (n_tiles > 1) publish(1, tb_, ok_b);
+  if (stager) {
+    publish(0, ta, ok_a);
+    if (n_tiles > 1) publish(1, tb_, ok_b);
+  }
   __syncthreads();  // every wave has its query and published its first V exponents: tiles go to the buffers
 
   // ---- stage this wave's sub-tile of tile i in buffer buf
@@ -520,21 +530,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
     return e_prev;
   };
   float e_stg = tile_exponent(0, kNoMag);  // E of the last staged tile
-  stage(0, ta, ok_a, 0, e_stg);
+  if (stager) stage(0, ta, ok_a, 0, e_stg);
   __syncthreads();
 #pragma unroll 1
   for (int i = 0;; ++i) {
     const float e_tile = e_stg;
     if (i + 1 < n_tiles) {
       e_stg = tile_exponent(i + 1, e_stg);
-      stage(i + 1, tb_, ok_b, (i + 1) & 1, e_stg);
+      if (stager) stage(i + 1, tb_, ok_b, (i + 1) & 1, e_stg);
     }
     SubTile tc = {};
     bool ok_c = false;
-    if (i + 2 < n_tiles) tc = fetch(i + 2, ok_c);
+    if (stager && i + 2 < n_tiles) tc = fetch(i + 2, ok_c);
     compute(i, i & 1, e_tile);
     if (i + 1 >= n_tiles) break;
-    if (i + 2 < n_tiles) publish(i + 2, tc, ok_c);
+    if (stager && i + 2 < n_tiles) publish(i + 2, tc, ok_c);
     __syncthreads();
     tb_ = tc;
     ok_b = ok_c;
@@ -582,8 +592,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void chunk_attention_kerne
 
 bool chunk_attention_shape(int64_t batch, int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads) {
   const int64_t cols = static_cast<int64_t>(max_q_len) * (num_q_heads / num_kv_heads);
-  const int64_t blocks = (cols + kColsWg - 1) / kColsWg * num_kv_heads * batch;
-  return cols >= kColsWg && blocks >= 256 && blocks * 64 * kWaves < (int64_t{1} << 31);
+  const int64_t blocks = (cols + kColsSel - 1) / kColsSel * num_kv_heads * batch;
+  return cols >= kColsSel && blocks >= 256 && blocks * 64 * kWavesWg < (int64_t{1} << 31);
 }
 
 bool chunk_attention_applies(const DecodeArgs& a) {
@@ -594,8 +604,8 @@ hipError_t launch_chunk_attention(const DecodeArgs& a, hipStream_t stream) {
   const int64_t cols = static_cast<int64_t>(a.q_len_max) * (a.num_q_heads / a.num_kv_heads);
   const int64_t n_wg = (cols + kColsWg - 1) / kColsWg * a.num_kv_heads * a.batch;  // < 2^31: checked by the caller
   const dim3 grid(static_cast<unsigned>(n_wg));
-  if (a.bits == 4) hipLaunchKernelGGL(chunk_attention_kernel<4>, grid, dim3(64 * kWaves), 0, stream, a);
-  else hipLaunchKernelGGL(chunk_attention_kernel<2>, grid, dim3(64 * kWaves), 0, stream, a);
+  if (a.bits == 4) hipLaunchKernelGGL(chunk_attention_kernel<4>, grid, dim3(64 * kWavesWg), 0, stream, a);
+  else hipLaunchKernelGGL(chunk_attention_kernel<2>, grid, dim3(64 * kWavesWg), 0, stream, a);
   return hipGetLastError();
 }
 

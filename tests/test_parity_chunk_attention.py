@@ -1,6 +1,6 @@
 """GPU parity of kvq_paged_prefill_attention on large chunks - at least 128 (query, head) columns
-per KV head and 256 workgroups of them, where the library dequantizes each cache tile once per
-128 columns into LDS (fp16 operands on the matrix cores) - against the oracle's multi-query
+per KV head and 256 blocks of them, where the library dequantizes each cache tile once per 256
+columns into LDS (fp16 operands on the matrix cores) - against the oracle's multi-query
 attention: every query row of every sequence in the fixed cases, sampled rows in the seeded
 random ones.
 
