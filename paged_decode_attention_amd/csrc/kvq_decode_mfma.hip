@@ -246,15 +246,17 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
   // that with a multiple of 8 items every split of an item lands on the same XCD (workgroups go to
   // the eight XCDs in turn) - and the merge of its partials, numbered alike, reads them from that
   // XCD's L2.
-  const uint32_t items = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads);
-  const uint32_t item = MQ ? 0u : blockIdx.x % items;
-  const int group = MQ ? 0 : static_cast<int>(blockIdx.x / items);  // split group (WG = 4) or split
+  // (scalar divisions by invariant divisors, see FastDiv)
+  const uint32_t gq = MQ ? 0u : fast_div(blockIdx.x, a.div_items);          // split group (WG = 4) or split
+  const uint32_t item = MQ ? 0u : blockIdx.x - gq * a.div_items.d;
+  const int group = static_cast<int>(gq);
   const int split = MQ ? static_cast<int>(blockIdx.x) : group * WG + wv;
-  const int kvh = MQ ? static_cast<int>(blockIdx.y % a.num_kv_heads)
-                     : static_cast<int>(item % static_cast<uint32_t>(a.num_kv_heads));
-  const int c0 = MQ ? 16 * static_cast<int>(blockIdx.y / a.num_kv_heads) : 0;  // first column of the tile
-  const int b = MQ ? static_cast<int>(blockIdx.z) : static_cast<int>(item / static_cast<uint32_t>(a.num_kv_heads));
-  const int g = a.num_q_heads / a.num_kv_heads;
+  const uint32_t hsel = MQ ? blockIdx.y : item;  // MQ: (column tile, KV head); else (sequence, KV head)
+  const uint32_t hq = fast_div(hsel, a.div_kvh);
+  const int kvh = static_cast<int>(hsel - hq * a.div_kvh.d);
+  const int c0 = MQ ? 16 * static_cast<int>(hq) : 0;  // first column of the tile
+  const int b = MQ ? static_cast<int>(blockIdx.z) : static_cast<int>(hq);
+  const int g = a.group;
   const int ps = PS16 ? 16 : a.page_size;
   const int tiles_per_page = PS16 ? 1 : ps / 16;
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
@@ -757,30 +759,32 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
 // loaded with independent loads before any is combined, so 32 splits cost one memory round trip.
 // The four groups' running (max, sum, vector) are then combined across rows, rotated back and
 // stored by row group 0.
+template <int NB>
 __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const int G = lane >> 4;
   const int n = lane & 15;
   // one query per sequence: numbered like the decode's items (item fastest, then the group's head)
   uint32_t pair = blockIdx.x;  // (b * q_len_max + j) * num_q_heads + h  (decode: q_len_max = 1)
+  uint32_t bb = 0;             // the sequence (decode)
   if (!a.q_lens) {
-    const uint32_t items = static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads);
-    const uint32_t gq = static_cast<uint32_t>(a.num_q_heads / a.num_kv_heads);
-    const uint32_t item = blockIdx.x % items, j = blockIdx.x / items;
-    const uint32_t bb = item / static_cast<uint32_t>(a.num_kv_heads), kk = item % static_cast<uint32_t>(a.num_kv_heads);
-    pair = bb * static_cast<uint32_t>(a.num_q_heads) + kk * gq + j;
+    const uint32_t j = fast_div(blockIdx.x, a.div_items);
+    const uint32_t item = blockIdx.x - j * a.div_items.d;
+    bb = fast_div(item, a.div_kvh);
+    const uint32_t kk = item - bb * a.div_kvh.d;
+    pair = bb * static_cast<uint32_t>(a.num_q_heads) + kk * static_cast<uint32_t>(a.group) + j;
   }
   const int q_len_max = a.q_lens ? a.q_len_max : 1;
   const int64_t pairs = static_cast<int64_t>(a.batch) * q_len_max * a.num_q_heads;
   const float2* ml_all = reinterpret_cast<const float2*>(a.ws_ml);
-  // One batch of 32 splits: row group G loads splits s0 + G + 4j (past s_last: s_last again).
+  // One batch of 4 NB splits: row group G loads splits s0 + G + 4j (past s_last: s_last again).
   struct Batch {
-    float2 ml[8];
-    float4 xa[8], xb[8];
+    float2 ml[NB];
+    float4 xa[NB], xb[NB];
   };
   auto load_batch = [&](int s0, int s_last, Batch& bt) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int sp = min(s0 + G + 4 * j, s_last);
       const int64_t row = sp * pairs + pair;
       bt.ml[j] = ml_all[row];
@@ -796,7 +800,8 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   load_batch(0, a.num_splits - 1, bt);
   __builtin_amdgcn_sched_barrier(0);
 
-  const int b = static_cast<int>(pair / static_cast<uint32_t>(q_len_max * a.num_q_heads));
+  const int b = a.q_lens ? static_cast<int>(pair / static_cast<uint32_t>(q_len_max * a.num_q_heads))
+                         : static_cast<int>(bb);
   const int len = min(max(ro_load(a.context_lens, b), 0), a.max_context_len);
   const int n_pages = (len + a.page_size - 1) / a.page_size;
   int nu = a.all_splits ? a.num_splits : min(a.num_splits, (n_pages + a.pages_per_split - 1) / a.pages_per_split);
@@ -807,10 +812,10 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
   const LaneFwht lf = lane_fwht(a.rot, n);
   float mo = kNegInf, lsum = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0;;) {
-    bool use[8];
+    bool use[NB];
     float mc = mo;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       // a split with no token for this row (several queries: past a query's causal limit) has
       // maximum -inf and weighs nothing (even when every split so far is such a split)
       use[j] = s0 + G + 4 * j < nu && bt.ml[j].x != kNegInf;
@@ -821,7 +826,7 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
 #pragma unroll
     for (int m = 0; m < 8; ++m) o[m] *= r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       if (!use[j]) continue;
       const float f = __builtin_amdgcn_exp2f(bt.ml[j].x - mc);
       lsum = __builtin_fmaf(bt.ml[j].y, f, lsum);
@@ -831,7 +836,7 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
       o[6] = __builtin_fmaf(bt.xb[j].z, f, o[6]); o[7] = __builtin_fmaf(bt.xb[j].w, f, o[7]);
     }
     mo = mc;
-    s0 += 32;
+    s0 += 4 * NB;
     if (s0 >= nu) break;
     load_batch(s0, nu - 1, bt);
   }
@@ -869,7 +874,15 @@ hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
 // Column tiles of 16 (query, head) pairs per KV head for several queries per sequence.
 int32_t mq_column_tiles(int32_t q_len_max, int32_t group) { return (q_len_max * group + 15) / 16; }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+static void set_index_divisors(DecodeArgs& a) {
+  a.div_items = make_fast_div(static_cast<uint32_t>(a.batch) * static_cast<uint32_t>(a.num_kv_heads));
+  a.div_kvh = make_fast_div(static_cast<uint32_t>(a.num_kv_heads));
+  a.group = a.num_q_heads / a.num_kv_heads;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& args, hipStream_t stream) {
+  DecodeArgs a = args;
+  set_index_divisors(a);
   const unsigned tiles = a.q_lens ? static_cast<unsigned>(mq_column_tiles(a.q_len_max, a.num_q_heads / a.num_kv_heads)) : 1u;
   const dim3 grid = a.q_lens ? dim3(static_cast<unsigned>(a.num_splits), static_cast<unsigned>(a.num_kv_heads) * tiles,
                                     static_cast<unsigned>(a.batch))
@@ -902,9 +915,16 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   return launch_decode_merge(a, stream);
 }
 
-hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode_merge(const DecodeArgs& args, hipStream_t stream) {
+  DecodeArgs a = args;
+  set_index_divisors(a);
   const int64_t pairs = static_cast<int64_t>(a.batch) * (a.q_lens ? a.q_len_max : 1) * a.num_q_heads;
-  hipLaunchKernelGGL(decode_merge_splits_kernel, dim3(static_cast<unsigned>(pairs)), dim3(64), 0, stream, a);
+  const dim3 grid(static_cast<unsigned>(pairs));
+  // the loads of one batch cover every partial row when there are at most 4 NB of them
+  if (a.num_splits <= 4) hipLaunchKernelGGL(decode_merge_splits_kernel<1>, grid, dim3(64), 0, stream, a);
+  else if (a.num_splits <= 8) hipLaunchKernelGGL(decode_merge_splits_kernel<2>, grid, dim3(64), 0, stream, a);
+  else if (a.num_splits <= 16) hipLaunchKernelGGL(decode_merge_splits_kernel<4>, grid, dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL(decode_merge_splits_kernel<8>, grid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -47,6 +47,31 @@ struct AppendArgs {
   int32_t token_scale;
 };
 
+// Division of 32-bit unsigned integers by an invariant divisor d >= 1 (Granlund-Montgomery,
+// round-up multiplier): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (t + ((n - t) >> s1)) >> s2, t = umulhi(n, m), s1 = min(l, 1), s2 = max(l - 1, 0), for
+// every n < 2^32. Kernels take the divisor uniform across the grid, so the steps are scalar.
+struct FastDiv {
+  uint32_t d, m;
+  int32_t s1, s2;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+  int l = 0;
+  while ((uint64_t{1} << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.m = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  const uint32_t t = __umulhi(n, f.m);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 struct DecodeArgs {
   const uint16_t* q;
   int32_t q_prerotated;
@@ -93,6 +118,10 @@ struct DecodeArgs {
   // Merge: every split of every row holds a partial (an empty one has maximum -inf), instead of
   // the splits that cover the row's pages.
   int32_t all_splits;
+  // Set by the launchers from the fields above (callers leave them): division by batch *
+  // num_kv_heads and by num_kv_heads, and the query heads per KV head.
+  FastDiv div_items, div_kvh;
+  int32_t group;
 };
 
 // Per-channel pages (the per-channel reading of OScaR): codes as in the token-wise cache, a
