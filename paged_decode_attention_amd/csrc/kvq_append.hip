@@ -262,10 +262,11 @@ __global__ __launch_bounds__(256, KVQ_APPEND_MIN_WAVES) void append_kernel(const
   const int lane = threadIdx.x & 63;
   const int G = lane >> 4;
   const int c = lane & 15;
-  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6);
-  const uint32_t H = static_cast<uint32_t>(a.num_kv_heads);
-  const int64_t tile = w / H;
-  const int h = static_cast<int>(w % H);
+  // work item w = (16-token tile, head), uniform per wave: scalar index arithmetic
+  const uint32_t w = blockIdx.x * 4u + static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)));
+  const uint32_t tq = fast_div(w, a.div_heads);
+  const int64_t tile = tq;
+  const int h = static_cast<int>(w - tq * a.div_heads.d);
   if (tile >= num_tiles || h >= a.num_kv_heads) return;  // uniform per wave
   const v4u bop[2] = {load_b<LB>(lane, 0), load_b<LB>(lane, 1)};
   TileInputs in;
@@ -299,7 +300,9 @@ hipError_t launch_lb(const AppendArgs& a, int lb, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+hipError_t launch_append(const AppendArgs& args, hipStream_t stream) {
+  AppendArgs a = args;
+  a.div_heads = make_fast_div(static_cast<uint32_t>(a.num_kv_heads));
   int lb = 0;
   while ((1 << lb) < a.rot.hb) ++lb;
   if (a.bits == 4 && !a.token_scale) return launch_lb<4, false>(a, lb, stream);

@@ -27,26 +27,6 @@ struct RowFwhtPlan {
 };
 RowFwhtPlan make_row_fwht_plan(int32_t hb);
 
-struct AppendArgs {
-  const uint16_t* k;
-  const uint16_t* v;
-  int64_t k_stride, v_stride;     // elements between tokens
-  int64_t num_tokens;
-  int32_t num_kv_heads;
-  const int64_t* slots;
-  uint8_t* k_codes;
-  uint8_t* v_codes;
-  float* k_sz;
-  float* v_sz;
-  int64_t num_slots;              // num_pages * page_size (< 2^32)
-  int32_t page_size;
-  uint32_t ps_magic;              // slot / page_size = (hi + ((slot - hi) >> 1)) >> ps_shift,
-  int32_t ps_shift;               //   hi = umulhi(slot, ps_magic)  (32-bit slots)
-  RowFwhtPlan rot;                // the rotation (Hadamard block size and lane plan)
-  int32_t bits;
-  int32_t token_scale;
-};
-
 // Division of 32-bit unsigned integers by an invariant divisor d >= 1 (Granlund-Montgomery,
 // round-up multiplier): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
 // n / d = (t + ((n - t) >> s1)) >> s2, t = umulhi(n, m), s1 = min(l, 1), s2 = max(l - 1, 0), for
@@ -71,6 +51,27 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   const uint32_t t = __umulhi(n, f.m);
   return (t + ((n - t) >> f.s1)) >> f.s2;
 }
+
+struct AppendArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_stride, v_stride;     // elements between tokens
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  const int64_t* slots;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  float* k_sz;
+  float* v_sz;
+  int64_t num_slots;              // num_pages * page_size (< 2^32)
+  int32_t page_size;
+  uint32_t ps_magic;              // slot / page_size = (hi + ((slot - hi) >> 1)) >> ps_shift,
+  int32_t ps_shift;               //   hi = umulhi(slot, ps_magic)  (32-bit slots)
+  RowFwhtPlan rot;                // the rotation (Hadamard block size and lane plan)
+  int32_t bits;
+  int32_t token_scale;
+  FastDiv div_heads;              // division by num_kv_heads (set by launch_append)
+};
 
 struct DecodeArgs {
   const uint16_t* q;
