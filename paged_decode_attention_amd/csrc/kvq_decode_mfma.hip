@@ -434,13 +434,43 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
   // offset x + 0x808080 (in [0x708080, 0x908080]) its three bytes b_i are x's base-256 digits
   // shifted by 128, so limb l_i = b_i - 128 is byte b_i with the top bit flipped, and
   // x = (l2 * 256 + l1) * 256 + l0. Column n takes head h_l: the F tile slots share the query.
+  // qv[(j * 4 + r) * 4 + k] is the channel that MFMA j, register slot r, byte k of lane group G
+  // multiplies: the byte the K-code operand puts there (INT4: 32 G + 16 j + 8 (r >> 1) + 2 k + (r & 1),
+  // INT2: 32 G + 16 j + 4 k + r). Those are 16-byte runs of the staged row: eight 16-byte LDS reads.
+  // Columns past the group's heads take the last head's query (finite scores that are never stored).
   float qv[32];
+  {
+    const float* qrow = &qs[min(h_l, ncols - 1)][0];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (BITS == 4) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int h = 0; h < 2; ++h) {  // channels 32 G + 16 j + 8 h + 2 k + (r & 1), r = 2 h + (r & 1)
+          const float4 lo = *reinterpret_cast<const float4*>(qrow + 32 * G + 16 * j + 8 * h);
+          const float4 hi = *reinterpret_cast<const float4*>(qrow + 32 * G + 16 * j + 8 * h + 4);
+          const float c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = (h_l < ncols) ? qs[h_l][qk_channel<BITS>(G, j, r, k)] : 0.f;
+          for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) qv[(j * 4 + 2 * h + rr) * 4 + k] = c[2 * k + rr];
+        }
+      } else {  // channels 32 G + 16 j + 4 k + r
+        float c[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float4 x = *reinterpret_cast<const float4*>(qrow + 32 * G + 16 * j + 4 * e);
+          c[4 * e] = x.x;
+          c[4 * e + 1] = x.y;
+          c[4 * e + 2] = x.z;
+          c[4 * e + 3] = x.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) qv[(j * 4 + r) * 4 + k] = c[4 * k + r];
+      }
+    }
+  }
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qv[i]));

@@ -87,17 +87,6 @@ __device__ __forceinline__ void split_bf16(const float (&w)[4], uint32_t& hi01, 
   lo23 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[2])) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[3])) << 16);
 }
 
-// Channel of the query that MFMA j, register slot r, byte k of lane group G multiplies (it must
-// match the byte the K-code operand puts there).
-template <int BITS>
-__device__ __forceinline__ int qk_channel(int G, int j, int r, int k) {
-  if constexpr (BITS == 4) {
-    return 32 * G + 16 * j + 8 * (r >> 1) + 2 * k + (r & 1);
-  } else {
-    return 32 * G + 16 * j + 4 * k + r;
-  }
-}
-
 // K-code operand of one tile for MFMA j from the bytes this lane loaded (32 channels of one token).
 template <int BITS>
 __device__ __forceinline__ v4i k_operand(const uint4 w, int j) {
