@@ -540,17 +540,19 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
         s1[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L1[1], s1[u], 0, 0, 0);
         s2[u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k1, L2[1], s2[u], 0, 0, 0);
       }
+      if constexpr (F == 1) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = t0 + u;
-        const v4i s = (((s2[u] << 8) + s1[u]) << 8) + s0[u];
-        if (F == 1 || t % F == 0) {
-          sc[t / F] = s;
-        } else {
-          const bool mine = u_l == t % F;
+        for (int u = 0; u < 2; ++u) sc[t0 + u] = (((s2[u] << 8) + s1[u]) << 8) + s0[u];
+      } else {  // F = 2: the lane's own tile (slot u_l) picked limb by limb, then one combination
+        const bool second = u_l == 1;
+        v4i a0, a1, a2;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[t / F][i] = mine ? s[i] : sc[t / F][i];
+        for (int i = 0; i < 4; ++i) {
+          a0[i] = second ? s0[1][i] : s0[0][i];
+          a1[i] = second ? s1[1][i] : s1[0][i];
+          a2[i] = second ? s2[1][i] : s2[0][i];
         }
+        sc[t0 / 2] = (((a2 << 8) + a1) << 8) + a0;
       }
     }
 
@@ -585,8 +587,8 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
     float mt = sr[0];
 #pragma unroll
     for (int i = 1; i < P; ++i) mt = fmaxf(mt, sr[i]);
-    mt = max_over_rows(mt);
-    if constexpr (F == 2) mt = fmaxf(mt, row_ror<8>(mt));
+    mt = max_over_rows_nc(mt);
+    if constexpr (F == 2) mt = max_nc(mt, row_ror<8>(mt));
     mt *= inv_scale;  // log2 units
     if (__any(mt > m_run + lazy)) {
       const float m_new = (mt > m_run + lazy) ? mt : m_run;

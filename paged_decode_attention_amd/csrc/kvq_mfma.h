@@ -12,6 +12,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 inline constexpr float kNegInf = -__builtin_inff();
 
@@ -30,6 +32,20 @@ __device__ __forceinline__ float max_over_rows(float v) {
   v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
   const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Maximum of two values that are finite or -inf (scores), as the median of (a, b, +inf): one
+// instruction, where fmaxf of values fresh from a lane exchange first quiets both operands.
+__device__ __forceinline__ float max_nc(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_inff());
+}
+
+// max_over_rows for scores (finite or -inf).
+__device__ __forceinline__ float max_over_rows_nc(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = max_nc(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max_nc(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 __device__ __forceinline__ float min_over_rows(float v) {
@@ -75,16 +91,17 @@ __device__ __forceinline__ uint32_t bias_bf16_hi(uint32_t lo_bytes) {
 __device__ __forceinline__ void split_bf16(const float (&w)[4], uint32_t& hi01, uint32_t& hi23, uint32_t& lo01,
                                            uint32_t& lo23) {
   uint32_t hb[4];
-  __bf16 lb[4];
+  float lf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     hb[i] = __float_as_uint(w[i]) & 0xFFFF0000u;
-    lb[i] = static_cast<__bf16>(w[i] - __uint_as_float(hb[i]));
+    lf[i] = w[i] - __uint_as_float(hb[i]);
   }
   hi01 = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
   hi23 = __builtin_amdgcn_perm(hb[3], hb[2], 0x07060302u);
-  lo01 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[0])) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[1])) << 16);
-  lo23 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[2])) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb[3])) << 16);
+  // the remainders rounded to bf16 two at a time (one packed conversion per pair)
+  lo01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lf[0], lf[1]}, v2bf));
+  lo23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lf[2], lf[3]}, v2bf));
 }
 
 // K-code operand of one tile for MFMA j from the bytes this lane loaded (32 channels of one token).
