@@ -5,7 +5,7 @@
 //
 // One wave per (split, KV head, sequence) - four splits of one (sequence, KV head) to a workgroup
 // when a sequence has 16 splits or more; the split's pages are walked as 16-token tiles, two
-// tiles per step. Dequantization is folded around the contractions instead of materialised:
+// tiles per step (four for INT2). Dequantization is folded around the contractions instead of materialised:
 //   score_j = q~ . (delta_j c_j + z_j 1) = delta_j (q~ . c_j) + z_j sum(q~)
 //   sum_j p_j v_j = sum_j (p_j delta_j) c_j + sum_j p_j z_j 1
 // so the integer codes c_j enter the MFMAs directly.
@@ -32,6 +32,9 @@
 #include "kvq_launch.h"
 #include "kvq_mfma.h"
 
+#ifndef KVQ_DECODE_NT2
+#define KVQ_DECODE_NT2 4      // tiles per step of the INT2 decode (one query per sequence)
+#endif
 #ifndef KVQ_DECODE_MIN_WAVES
 #define KVQ_DECODE_MIN_WAVES 2    // waves per SIMD the register allocation must allow
 #endif
@@ -207,7 +210,10 @@ __device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], i
 // MQ = true: several queries per sequence (F = 1); a wave takes a tile of 16 columns out of the
 // (query token, head) pairs of one KV head, column c meaning query c / g, head c % g, each with
 // its own causal length.
-// NT = 2 tiles per step, three step buffers.
+// NT = 2 tiles per step (INT4, and several queries per sequence) or 4 (INT2 with one query per
+// sequence: its tiles are half the registers, and the per-step softmax bookkeeping - the maximum
+// across rows, the rescale test, the scale/zero staging - is spent once per 64 tokens), three step
+// buffers.
 // WG = 4 (one query per sequence, a sequence in many splits): a workgroup holds the WG splits
 // 4 j .. 4 j + 3 of one (sequence, KV head) item, one per wave. Each wave walks its own pages as
 // above; at the end the waves combine their (maximum, sum, accumulator) rows in LDS (log-sum-exp),
@@ -216,7 +222,7 @@ __device__ __forceinline__ void lse_combine(float& m, float& l, float (&o)[8], i
 template <int BITS, bool PS16, int NT, bool MQ, int F, int WG>
 __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_kernel(const DecodeArgs a) {
   static_assert(F == 1 || F == 2, "pack factor");
-  static_assert(NT == 2, "a step is one PV chunk of two tiles");
+  static_assert(NT == 2 || (NT == 4 && !MQ), "a step is one or two PV chunks of two tiles");
   static_assert(!MQ || F == 1, "several queries fill the 16 columns themselves");
   static_assert(WG == 1 || (!MQ && F == 2 && WG == 4), "split groups: one query per sequence");
   constexpr int W = 16 / F;   // columns per tile slot
@@ -887,7 +893,7 @@ __global__ __launch_bounds__(64) void decode_merge_splits_kernel(const DecodeArg
 
 constexpr int kMinSplitsGrouped = 16;
 
-template <bool MQ, int F, int NT, int WG>
+template <bool MQ, int F, int NT, int WG, int NT2 = NT>
 hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   const bool ps16 = a.page_size == 16;
   const dim3 block(64 * WG);
@@ -895,8 +901,8 @@ hipError_t launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
     if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<4, true, NT, MQ, F, WG>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((decode_mfma_kernel<4, false, NT, MQ, F, WG>), grid, block, 0, stream, a);
   } else {
-    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, NT, MQ, F, WG>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, NT, MQ, F, WG>), grid, block, 0, stream, a);
+    if (ps16) hipLaunchKernelGGL((decode_mfma_kernel<2, true, NT2, MQ, F, WG>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mfma_kernel<2, false, NT2, MQ, F, WG>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -934,7 +940,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& args, hipStream_t stream) {
   const uint64_t items = static_cast<uint64_t>(a.batch) * static_cast<uint64_t>(a.num_kv_heads);
   const uint64_t groups = (static_cast<uint64_t>(a.num_splits) + 3) / 4;
   if (a.num_splits >= kMinSplitsGrouped && groups * items * 256 < (uint64_t{1} << 32)) {
-    const hipError_t e = launch_kernel<false, 2, 2, 4>(a, dim3(static_cast<unsigned>(groups * items)), stream);
+    const hipError_t e = launch_kernel<false, 2, 2, 4, KVQ_DECODE_NT2>(a, dim3(static_cast<unsigned>(groups * items)), stream);
     if (e != hipSuccess) return e;
     // the merge sees one partial per group, every group's row written (an empty one with maximum -inf)
     DecodeArgs m = a;
@@ -942,7 +948,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& args, hipStream_t stream) {
     m.all_splits = 1;
     return launch_decode_merge(m, stream);
   }
-  const hipError_t e = launch_kernel<false, 2, 2, 1>(a, grid, stream);
+  const hipError_t e = launch_kernel<false, 2, 2, 1, KVQ_DECODE_NT2>(a, grid, stream);
   if (e != hipSuccess || a.num_splits == 1) return e;
   return launch_decode_merge(a, stream);
 }
