@@ -93,10 +93,10 @@ def decode_bytes(lens, num_q_heads: int, num_kv_heads: int, bits: int, page_size
 
 CSRC = os.path.join(ROOT, "paged_decode_attention_amd", "csrc")
 KERNEL_SOURCES = {
-    "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
-    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
-    "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
-    "chunk_attention_kernel": ["kvq_chunk_attn.hip", "kvq_chunk.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h"],
+    "append_kernel": ["kvq_append.hip", "kvq_rotate_mfma.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "kvq_fastdiv.h"],
+    "decode_mfma_kernel": ["kvq_decode_mfma.hip", "kvq_decode.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "kvq_fastdiv.h"],
+    "decode_merge_splits_kernel": ["kvq_decode_mfma.hip", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "kvq_fastdiv.h"],
+    "chunk_attention_kernel": ["kvq_chunk_attn.hip", "kvq_chunk.h", "kvq_mfma.h", "kvq_device.h", "kvq_launch.h", "kvq_fastdiv.h"],
 }
 CALIBRATION_BYTES = 256 << 20
 TRAFFIC_TAG = "traffic-json: "

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvq_fastdiv.h"
+
 namespace kvq {
 
 constexpr int kHeadDim = 128;
@@ -26,31 +28,6 @@ struct RowFwhtPlan {
   uint64_t pos;          // 4 bits per lane: output channel block (channels 8 pos .. 8 pos + 7)
 };
 RowFwhtPlan make_row_fwht_plan(int32_t hb);
-
-// Division of 32-bit unsigned integers by an invariant divisor d >= 1 (Granlund-Montgomery,
-// round-up multiplier): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
-// n / d = (t + ((n - t) >> s1)) >> s2, t = umulhi(n, m), s1 = min(l, 1), s2 = max(l - 1, 0), for
-// every n < 2^32. Kernels take the divisor uniform across the grid, so the steps are scalar.
-struct FastDiv {
-  uint32_t d, m;
-  int32_t s1, s2;
-};
-
-inline FastDiv make_fast_div(uint32_t d) {
-  int l = 0;
-  while ((uint64_t{1} << l) < d) ++l;
-  FastDiv f;
-  f.d = d;
-  f.m = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
-  f.s1 = l < 1 ? l : 1;
-  f.s2 = l > 1 ? l - 1 : 0;
-  return f;
-}
-
-__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
-  const uint32_t t = __umulhi(n, f.m);
-  return (t + ((n - t) >> f.s1)) >> f.s2;
-}
 
 struct AppendArgs {
   const uint16_t* k;
