@@ -1151,7 +1151,7 @@ def suite_multi_query(dev, stream, cpu):
         rows.append(_line(workload=f"{name} shape, {qlen} queries per sequence "
                                    f"({'speculative verification' if qlen < 16 else 'chunked-prefill chunk'})",
                           batch=shape.batch, queries_per_seq=qlen,
-                          kernel="large-chunk (tiles staged per 128 columns)" if chunk else "split (16-column tiles)",
+                          kernel="large-chunk (tiles staged per 256 columns)" if chunk else "split (16-column tiles)",
                           attention_ms=round(ms, 5), cache_read_GBps=round(nbytes / ms / 1e6, 1),
                           query_tokens_per_s=round(shape.batch * qlen / (ms * 1e-3), 1), **rates))
         del caches
