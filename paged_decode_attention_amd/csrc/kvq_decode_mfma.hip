@@ -793,8 +793,9 @@ __global__ __launch_bounds__(64 * WG, KVQ_DECODE_MIN_WAVES) void decode_mfma_ker
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, query head) per wave. Row group G
-// takes splits G, G + 4, G + 8, ...; lane n holds channels 8n..8n+7. Eight splits per group are
-// loaded with independent loads before any is combined, so 32 splits cost one memory round trip.
+// takes splits G, G + 4, G + 8, ...; lane n holds channels 8n..8n+7. NB splits per row group (1, 2,
+// 4 or 8: as many as the call's partial rows need, at most eight) are loaded with independent loads
+// before any is combined, so up to 4 NB splits cost one memory round trip.
 // The four groups' running (max, sum, vector) are then combined across rows, rotated back and
 // stored by row group 0.
 template <int NB>
