@@ -55,25 +55,32 @@ __device__ __forceinline__ void quantize_tile(v4f (&y)[8], int c, uint32_t (&pac
   }
   float s[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (TOKEN_SCALE) {
-    // RMS in double precision across the 128 channels (16 lanes x 8), rounded once to float.
-    bool plain = true;
+    // RMS in double precision across the 128 channels (16 lanes x 8), rounded once to float. The
+    // row sums are equal in the row's 16 lanes (butterfly of commutative adds), so lane c takes the
+    // square root and the reciprocal of token c & 3 only, and the quads broadcast them.
+    double ss[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      double ss = 0.0;
+      double v = 0.0;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) ss += static_cast<double>(y[n][i]) * static_cast<double>(y[n][i]);
-      ss = row16_sum_f64(ss);
-      float si = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
-      if (si == 0.0f) si = 1.0f;
-      s[i] = si;
-      plain = plain && si >= kFastMinScale && si < kFastMaxScale;
+      for (int n = 0; n < 8; ++n) v += static_cast<double>(y[n][i]) * static_cast<double>(y[n][i]);
+      ss[i] = row16_sum_f64(v);
     }
-    if (__builtin_expect(__all(plain), 1)) {
+    float s_own = static_cast<float>(sqrt(pick4(c & 3, ss[0], ss[1], ss[2], ss[3]) * (1.0 / kHeadDim)));
+    if (s_own == 0.0f) s_own = 1.0f;
+    const bool plain_own = s_own >= kFastMinScale && s_own < kFastMaxScale;
+    const float rs_own = rcp_rn(plain_own ? s_own : 1.0f);
+    s[0] = quad_bcast<0>(s_own);
+    s[1] = quad_bcast<1>(s_own);
+    s[2] = quad_bcast<2>(s_own);
+    s[3] = quad_bcast<3>(s_own);
+    // every token of the wave is some lane's own token
+    if (__builtin_expect(__all(plain_own), 1)) {
+      const float rs[4] = {quad_bcast<0>(rs_own), quad_bcast<1>(rs_own), quad_bcast<2>(rs_own), quad_bcast<3>(rs_own)};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float rs = rcp_rn(s[i]);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], s[i], rs);
+        for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], s[i], rs[i]);
       }
     } else {
       // a subnormal, tiny or huge RMS somewhere in the wave: IEEE division for the whole wave (the
