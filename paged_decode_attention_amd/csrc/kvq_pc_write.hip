@@ -36,25 +36,32 @@ __device__ __forceinline__ void pc_quantize_tile(v4f (&y)[8], bool odd_lb, int c
 #pragma unroll
       for (int i = 0; i < 4; ++i) y[n][i] *= kInvSqrt2;
   }
-  // u = y / s per token, s = RMS (double precision across the 16-lane row, rounded once)
-  bool plain = true;
+  // u = y / s per token, s = RMS (double precision across the 16-lane row, rounded once). The row
+  // sums are equal in the row's 16 lanes, so lane c takes the square root and the reciprocal of
+  // token c & 3 only and the quads broadcast them.
+  double ss[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    double ss = 0.0;
+    double v = 0.0;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) ss += static_cast<double>(y[n][i]) * static_cast<double>(y[n][i]);
-    ss = row16_sum_f64(ss);
-    float si = static_cast<float>(sqrt(ss * (1.0 / kHeadDim)));
-    if (si == 0.0f) si = 1.0f;
-    s[i] = si;
-    plain = plain && si >= 0x1p-100f && si <= 0x1p100f;
+    for (int n = 0; n < 8; ++n) v += static_cast<double>(y[n][i]) * static_cast<double>(y[n][i]);
+    ss[i] = row16_sum_f64(v);
   }
-  if (__builtin_expect(__all(plain), 1)) {
+  float s_own = static_cast<float>(sqrt(pick4(c & 3, ss[0], ss[1], ss[2], ss[3]) * (1.0 / kHeadDim)));
+  if (s_own == 0.0f) s_own = 1.0f;
+  const bool plain_own = s_own >= 0x1p-100f && s_own <= 0x1p100f;
+  const float rs_own = rcp_rn(plain_own ? s_own : 1.0f);
+  s[0] = quad_bcast<0>(s_own);
+  s[1] = quad_bcast<1>(s_own);
+  s[2] = quad_bcast<2>(s_own);
+  s[3] = quad_bcast<3>(s_own);
+  // every token of the wave is some lane's own token
+  if (__builtin_expect(__all(plain_own), 1)) {
+    const float rs[4] = {quad_bcast<0>(rs_own), quad_bcast<1>(rs_own), quad_bcast<2>(rs_own), quad_bcast<3>(rs_own)};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float rs = rcp_rn(s[i]);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], s[i], rs);
+      for (int n = 0; n < 8; ++n) y[n][i] = div_rn(y[n][i], s[i], rs[i]);
     }
   } else {
     // an extreme s and y are first brought near 1 by the same power of two (exact), so that the
